@@ -1,0 +1,216 @@
+/*
+ * pkv.h -- batched attention over a paged KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI: plain integers, host or device pointers and sizes.  No C++ or torch
+ * types cross it.  The operations follow the documentation pages of the mstar
+ * serving engine:
+ *   - mstar.engine.resources.attn.wrappers  (FlashInferDecodeWrapper,
+ *     FlashInferPrefillWrapper, FlashInferMixedWrapper: plan / run;
+ *     check_flashinfer_head_dim)
+ *   - mstar.engine.resources.kv.plan         (PagedIndptrs, SequenceView,
+ *     KVPlanOutput, PinnedIndexRing)
+ *   - mstar.engine.resources.attn.workspace  (Workspace: split-KV partials,
+ *     sizing, overflow reporting)
+ *   - mstar.engine.resources.attn.dense      (DenseAttentionManager: the
+ *     [prefix | fresh] sequence; requires_kv_write: write K/V, then run)
+ *
+ * Data layout
+ * -----------
+ * KV cache layer slice (wrappers module docstring; the run methods):
+ *     [max_pages, 2, page_size, num_kv_heads, head_dim]  bf16, contiguous.
+ *   Index 0 of the "2" axis is K, index 1 is V (a convention: no page fixes it).
+ * q, out : [total_q, num_qo_heads, head_dim] bf16, contiguous (decode: total_q = batch).
+ * lse    : [total_q, num_qo_heads] float32, natural log of the sum of exp of the
+ *          scaled logits.  Optional (NULL: not written).
+ * k_new, v_new : [total_q, num_kv_heads, head_dim] bf16, contiguous.
+ * Page table (kv.plan, PagedIndptrs), host int32 arrays:
+ *   qo_indptr[batch+1]              query tokens of row r are q[qo_indptr[r] : qo_indptr[r+1]]
+ *   paged_kv_indptr[batch+1]        pages of row r are paged_kv_indices[indptr[r] : indptr[r+1]]
+ *   paged_kv_indices[indptr[batch]] physical page ids in [0, max_pages)
+ *   paged_kv_last_page_len[batch]   tokens on row r's last page, in [1, page_size]
+ *   so kv_len[r] = (pages(r) - 1) * page_size + last_page_len[r].
+ *
+ * Semantics
+ * ---------
+ * Query token t of row r sits at position p = kv_len - q_len + t of the row (the
+ * queries are the row's last tokens: a [cached prefix | fresh tokens] sequence,
+ * attn.dense).  It attends to keys j with lo <= j <= hi where hi = p when causal
+ * (else kv_len - 1) and lo = max(0, p - window_left) when window_left >= 0 (else
+ * 0): window_left counts the positions before the query that it still sees
+ * (FlashInferPrefillWrapper.plan; the decode plan takes the same argument).
+ * Query head h reads KV head h / (num_qo_heads / num_kv_heads).
+ *   out = softmax(q k^T / sqrt(head_dim)) v over the visible keys, fp32 accumulation.
+ *
+ * Call order per step (attn.dense requires_kv_write: the layer stores its K/V
+ * before it runs attention):
+ *   pkv_plan_create (or pkv_plan_update)    host only; never touches the device
+ *   pkv_plan_upload(workspace, stream)      async H2D from library-owned pinned memory
+ *   per layer: pkv_append_kv(...)           optional; stores this step's K/V
+ *              pkv_run(...)                 attention for every planned query
+ * One plan serves every layer of a step.
+ *
+ * Ownership: the caller owns every device buffer (q, out, lse, cache, workspace,
+ * k_new, v_new).  The library owns the plan handle, which copies what it needs
+ * from the host arrays (no pointer is kept after a call returns) and a depth-2
+ * ring of page-locked staging buffers (kv.plan, PinnedIndexRing).
+ *
+ * Errors: every call returns a pkv_status; pkv_last_error() returns a message
+ * for the calling thread's last failure (valid until that thread's next call).
+ * Device work is enqueued on the given stream and is never synchronised by the
+ * library, except that re-using a staging buffer waits for the copy that last
+ * read it.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_E_INVALID = 1,      /* malformed page table, bad argument, q_len > kv_len, kv_lens mismatch */
+  PKV_E_UNSUPPORTED = 2,  /* head_dim, dtype, page_size or group size this build does not compute */
+  PKV_E_WORKSPACE = 3,    /* workspace smaller than the plan needs; message gives the bytes */
+  PKV_E_CAPACITY = 4,     /* more prompt rows than max_prefill_rows (mixed step) */
+  PKV_E_CONFLICT = 5,     /* two appended tokens map to one cache slot */
+  PKV_E_DEVICE = 6,       /* a HIP runtime call failed; message gives the HIP error */
+  PKV_E_STATE = 7         /* call out of order (e.g. run before upload, or another workspace) */
+} pkv_status;
+
+typedef enum pkv_kind {
+  PKV_KIND_DECODE = 0,   /* one query token per row; qo_indptr is NULL (FlashInferDecodeWrapper) */
+  PKV_KIND_PREFILL = 1,  /* ragged query rows (FlashInferPrefillWrapper) */
+  PKV_KIND_MIXED = 2     /* one-token rows on a decode sub-plan, other rows on a prefill
+                            sub-plan (FlashInferMixedWrapper) */
+} pkv_kind;
+
+typedef enum pkv_dtype { PKV_DTYPE_BF16 = 0 } pkv_dtype;
+
+typedef struct pkv_plan_params {
+  int32_t kind;                 /* pkv_kind */
+  int32_t num_qo_heads;         /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;         /* Hk */
+  int32_t head_dim;             /* 64 or 128 (check_flashinfer_head_dim analogue) */
+  int32_t page_size;            /* power of two in [1, 256] */
+  int32_t causal;               /* prefill/mixed: nonzero = causal, aligned to the end of KV */
+  int32_t window_left;          /* -1 = unbounded, else >= 0 */
+  int32_t dtype;                /* PKV_DTYPE_BF16 */
+  int32_t max_prefill_rows;     /* mixed only: capacity of the prefill sub-plan */
+  int32_t num_cus;              /* compute units the plan balances over; 0 = ask the current HIP
+                                   device (the workspace page: plan size depends on the SM count) */
+  int64_t max_pages;            /* pages in the layer slice; page ids must be below it */
+  int32_t decode_tiles_per_cu;  /* split-KV target: at most this many decode tiles per CU; 0 = 16 */
+  int32_t decode_min_chunk_pages; /* smallest split-KV chunk, in pages; 0 = 8 */
+} pkv_plan_params;
+
+/* One unit of decode work: a row, a KV head and a contiguous key range.
+ * The tile covers keys [kv_start, kv_end) of the row; out_slot < 0 means the tile
+ * writes out/lse directly, else it writes split-KV partial number out_slot into
+ * the workspace and a merge combines the partials. */
+typedef struct pkv_decode_tile {
+  int32_t row, kv_head, kv_start, kv_end;
+  int32_t page_base;  /* paged_kv_indptr[row] */
+  int32_t q_index;    /* token index into q/out */
+  int32_t out_slot;   /* -1 or partial slot */
+  int32_t kv_len;     /* the row's kv_len */
+} pkv_decode_tile;
+
+/* One split-KV merge: partials [slot_base, slot_base + n_chunks) of (q_index, kv_head). */
+typedef struct pkv_merge_entry {
+  int32_t q_index, kv_head, slot_base, n_chunks;
+} pkv_merge_entry;
+
+/* One unit of prefill work: a row, a KV head and a block of that row's query tokens.
+ * Query rows of the block are q tokens [q_base + q_start, q_base + q_start + q_count)
+ * of every query head of kv_head's group.  Keys [kv_lo, kv_hi] (inclusive) cover the
+ * union of the block's visible ranges. */
+typedef struct pkv_prefill_tile {
+  int32_t row, kv_head, q_start, q_count;
+  int32_t kv_lo, kv_hi;
+  int32_t page_base;  /* paged_kv_indptr[row] */
+  int32_t q_base;     /* qo_indptr[row]: packed token index of the row's first query */
+  int32_t kv_len, q_len;
+  int32_t pad0, pad1;
+} pkv_prefill_tile;
+
+typedef struct pkv_plan pkv_plan;
+
+/* Fill *p with defaults: causal = 1, window_left = -1, dtype = bf16, tuning knobs 0. */
+void pkv_plan_params_init(pkv_plan_params* p);
+
+/* Validate the page table and build a plan (FlashInfer*Wrapper.plan analogue).
+ * Host only.  qo_indptr must be NULL for PKV_KIND_DECODE and non-NULL otherwise.
+ * kv_lens (optional, may be NULL) must equal the lengths the page table implies.
+ * On success *out owns a new plan and *workspace_bytes is the exact size of the
+ * device workspace the plan needs (plan metadata plus split-KV partials).
+ * Errors: PKV_E_INVALID, PKV_E_UNSUPPORTED, PKV_E_CAPACITY, PKV_E_CONFLICT, and
+ * PKV_E_DEVICE when num_cus == 0 and the device cannot be queried. */
+pkv_status pkv_plan_create(const pkv_plan_params* params, int32_t batch,
+                           const int32_t* qo_indptr, const int32_t* paged_kv_indptr,
+                           const int32_t* paged_kv_indices,
+                           const int32_t* paged_kv_last_page_len, const int32_t* kv_lens,
+                           pkv_plan** out, size_t* workspace_bytes);
+
+/* Re-plan an existing handle for a new step with the same params (keeps its staging
+ * ring).  Arguments and errors as pkv_plan_create; on error the old plan is kept. */
+pkv_status pkv_plan_update(pkv_plan* plan, int32_t batch, const int32_t* qo_indptr,
+                           const int32_t* paged_kv_indptr, const int32_t* paged_kv_indices,
+                           const int32_t* paged_kv_last_page_len, const int32_t* kv_lens,
+                           size_t* workspace_bytes);
+
+void pkv_plan_destroy(pkv_plan* plan);
+
+/* Inspection (host pointers owned by the plan, valid until the next update/destroy). */
+pkv_status pkv_plan_decode_tiles(const pkv_plan* plan, const pkv_decode_tile** tiles, int32_t* n);
+pkv_status pkv_plan_prefill_tiles(const pkv_plan* plan, const pkv_prefill_tile** tiles, int32_t* n);
+pkv_status pkv_plan_merges(const pkv_plan* plan, const pkv_merge_entry** merges, int32_t* n);
+/* Flat write slot page * page_size + offset of every planned query token, in q order
+ * (decode: the row's last page at offset last_page_len - 1;
+ *  FlashInferDecodeWrapper.plan, KVPlanOutput.decode_pages / decode_offsets). */
+pkv_status pkv_plan_write_slots(const pkv_plan* plan, const int64_t** slots, int32_t* n);
+/* Mixed step: packed q indices of the prompt tokens, prompt rows in ascending order
+ * ("moved to the front", FlashInferMixedWrapper).  n = 0 for other kinds. */
+pkv_status pkv_plan_permutation(const pkv_plan* plan, const int32_t** perm, int32_t* n);
+/* Scalars: [0] total_q, [1] batch, [2] decode rows, [3] prompt rows, [4] split-KV chunk
+ * pages, [5] partial slots, [6] metadata bytes, [7] workspace bytes, [8] num_cus used. */
+pkv_status pkv_plan_info(const pkv_plan* plan, int64_t info[16]);
+
+/* Copy the plan's metadata into the head of `workspace` (device memory of at least
+ * the plan's workspace_bytes) with hipMemcpyAsync on `stream` (a hipStream_t; NULL =
+ * the null stream) from a page-locked staging buffer.  The staging buffer the copy
+ * reads is reused only after that copy has completed (an event recorded behind it),
+ * so re-planning while earlier steps are in flight is safe (attn.dense
+ * force_double_buffer hazard).  PKV_E_WORKSPACE if workspace_bytes is too small. */
+pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention for every planned query (FlashInfer*Wrapper.run analogue).
+ * q, kv_cache_layer, out: device pointers (layouts above); lse may be NULL.
+ * workspace must be the buffer of the last pkv_plan_upload (else PKV_E_STATE).
+ * Decode rows whose keys span several chunks write fp32 partials into the
+ * workspace and a merge kernel combines them (attn.workspace).  Enqueued on stream. */
+pkv_status pkv_run(const pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
+                   float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Store this step's K and V of every planned query token at its write slot:
+ * cache[page, 0, off] = k_new[t], cache[page, 1, off] = v_new[t]
+ * (decode: at last_page_len - 1 of the last page; FlashInferDecodeWrapper.plan).
+ * Reads the slots from the uploaded workspace.  Enqueued on stream. */
+pkv_status pkv_append_kv(const pkv_plan* plan, const void* k_new, const void* v_new,
+                         void* kv_cache_layer, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

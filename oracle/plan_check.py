@@ -1,0 +1,160 @@
+"""Checks for the planner's integer output.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Two kinds of check:
+  * cover checks, which hold for any valid plan: decode tiles cover every
+    visible key of every (row, KV head) exactly once; prefill tiles cover every
+    (row, KV head, query token) exactly once with a key range containing that
+    token's visible keys; split-KV partial slots are unique and merged once;
+  * a restatement of the documented tiling policy in plain Python (the pages
+    say only that a plan's size depends on rows, heads and the CU count,
+    mstar.engine.resources.attn.workspace, Workspace), so the planner's tile
+    lists can be compared bit for bit.
+
+Policy (the same rules the header documents):
+  decode rows   visible keys [lo, N-1]; pages fp = lo // ps .. lp = (N-1) // ps.
+                chunk = min_chunk_pages * 2^k, the smallest with
+                Hk * sum_r ceil(pages_r / chunk) <= tiles_per_cu * num_cus, or
+                the first reaching the longest row.  Rows sorted by visible pages
+                descending (ties: row index); per row chunk-major, head-minor.
+                Rows with more than one chunk get Hk * n_chunks consecutive
+                partial slots, head-major.
+  prefill rows  blocks of 128 // group query tokens; per block keys
+                [lo(first token), hi(last token)]; tiles sorted by key count
+                descending, ties by (row, block, head).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .reference import decode_csr, query_position, visible_keys
+
+__all__ = ["decode_policy", "prefill_policy", "check_decode_cover", "check_prefill_cover",
+           "split_rows"]
+
+
+def split_rows(kind, layout, max_prefill_rows=0):
+    """Which rows go to the decode plan and which to the prefill plan."""
+    if kind == "decode":
+        return [r for r in range(len(layout))], []
+    if kind == "prefill":
+        return [], [r for r, l in enumerate(layout) if l.q_len >= 1]
+    dec = [r for r, l in enumerate(layout) if l.q_len == 1]
+    pre = [r for r, l in enumerate(layout) if l.q_len >= 2]
+    if len(pre) > max_prefill_rows:
+        raise ValueError("more prompt rows than max_prefill_rows")
+    return dec, pre
+
+
+def decode_policy(layout, rows, *, page_size, num_kv_heads, window_left, num_cus, qo_indptr,
+                  kv_indptr, tiles_per_cu=16, min_chunk_pages=8):
+    """Expected decode tiles and merges.
+
+    Returns (tiles, merges, chunk_pages, n_slots) with tiles as tuples
+    (row, kv_head, kv_start, kv_end, page_base, q_index, out_slot, kv_len) and
+    merges as (q_index, kv_head, slot_base, n_chunks).
+    """
+    ps = page_size
+    info = {}
+    for r in rows:
+        n = layout[r].kv_len
+        lo, _ = visible_keys(n - 1, n, True, window_left)
+        fp, lp = lo // ps, (n - 1) // ps
+        info[r] = (lo, fp, lp, lp - fp + 1)
+    chunk = min_chunk_pages
+    if rows:
+        longest = max(v[3] for v in info.values())
+        budget = tiles_per_cu * num_cus
+
+        def count(c):
+            return num_kv_heads * sum(-(-v[3] // c) for v in info.values())
+
+        while chunk < longest and count(chunk) > budget:
+            chunk *= 2
+    order = sorted(rows, key=lambda r: (-info[r][3], r))
+    tiles, merges = [], []
+    slot = 0
+    for r in order:
+        lo, fp, lp, vis = info[r]
+        n = layout[r].kv_len
+        nch = -(-vis // chunk)
+        base = slot if nch > 1 else -1
+        for i in range(nch):
+            ks = max(lo, (fp + i * chunk) * ps)
+            ke = min(n, (fp + (i + 1) * chunk) * ps)
+            for hk in range(num_kv_heads):
+                out_slot = base + hk * nch + i if nch > 1 else -1
+                tiles.append((r, hk, ks, ke, int(kv_indptr[r]), int(qo_indptr[r]), out_slot, n))
+        if nch > 1:
+            for hk in range(num_kv_heads):
+                merges.append((int(qo_indptr[r]), hk, base + hk * nch, nch))
+            slot += num_kv_heads * nch
+    return tiles, merges, chunk, slot
+
+
+def prefill_policy(layout, rows, *, num_qo_heads, num_kv_heads, causal, window_left, qo_indptr,
+                   kv_indptr):
+    """Expected prefill tiles as tuples
+    (row, kv_head, q_start, q_count, kv_lo, kv_hi, page_base, q_base, kv_len, q_len)."""
+    group = num_qo_heads // num_kv_heads
+    bt = 128 // group
+    items = []
+    for r in rows:
+        n, L = layout[r].kv_len, layout[r].q_len
+        for b in range(-(-L // bt)):
+            qs = b * bt
+            qc = min(bt, L - qs)
+            lo, _ = visible_keys(query_position(n, L, qs), n, causal, window_left)
+            _, hi = visible_keys(query_position(n, L, qs + qc - 1), n, causal, window_left)
+            for hk in range(num_kv_heads):
+                items.append(((-(hi - lo + 1), r, b, hk),
+                              (r, hk, qs, qc, lo, hi, int(kv_indptr[r]), int(qo_indptr[r]), n, L)))
+    items.sort(key=lambda x: x[0])
+    return [t for _, t in items]
+
+
+def check_decode_cover(tiles, merges, layout, rows, *, num_kv_heads, window_left, n_slots):
+    """Every visible key of every (decode row, KV head) in exactly one tile;
+    partial slots unique, in range, and merged exactly once in chunk order."""
+    seen = {}
+    slots = set()
+    for (r, hk, ks, ke, _pb, _qi, slot, _n) in tiles:
+        assert 0 <= ks < ke, (r, hk, ks, ke)
+        seen.setdefault((r, hk), []).append((ks, ke, slot))
+        if slot >= 0:
+            assert slot not in slots and slot < n_slots
+            slots.add(slot)
+    assert set(seen) == {(r, hk) for r in rows for hk in range(num_kv_heads)}
+    merged = set()
+    mslots = {}
+    for (qi, hk, base, nch) in merges:
+        assert nch > 1
+        mslots[(qi, hk)] = list(range(base, base + nch))
+        merged.update(range(base, base + nch))
+    assert merged == slots
+    for (r, hk), parts in seen.items():
+        n = layout[r].kv_len
+        lo, hi = visible_keys(n - 1, n, True, window_left)
+        parts.sort()
+        assert parts[0][0] == lo and parts[-1][1] == hi + 1
+        for a, b in zip(parts, parts[1:]):
+            assert a[1] == b[0]
+        if len(parts) > 1:
+            assert all(p[2] >= 0 for p in parts)
+        else:
+            assert parts[0][2] == -1
+
+
+def check_prefill_cover(tiles, layout, rows, *, num_kv_heads, causal, window_left):
+    """Every (prefill row, KV head, query token) in exactly one tile, whose key
+    range contains that token's visible keys."""
+    count = {}
+    for (r, hk, qs, qc, klo, khi, _pb, _qb, n, L) in tiles:
+        assert qc >= 1 and 0 <= qs and qs + qc <= L
+        for t in range(qs, qs + qc):
+            lo, hi = visible_keys(query_position(n, L, t), n, causal, window_left)
+            assert klo <= lo and hi <= khi, (r, t, lo, hi, klo, khi)
+            count[(r, hk, t)] = count.get((r, hk, t), 0) + 1
+    want = {(r, hk, t) for r in rows for hk in range(num_kv_heads) for t in range(layout[r].q_len)}
+    assert set(count) == want and all(v == 1 for v in count.values())
