@@ -1,0 +1,269 @@
+"""Benchmark: batched attention over a paged KV cache on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--config NAME] [--no-cpu-baseline]
+                    [--no-secondary]
+
+A step is one pass of the whole hot path over one batch of synthetic input that
+is already resident in HBM: host re-plan of the page table (pkv_plan_update),
+upload of the plan metadata, KV append of this step's token (decode workloads),
+and attention (decode + split-KV merge, prefill, or both for the mixed step).
+
+The headline workload is batched GQA decode with append: 128 requests,
+32 query heads over 8 KV heads, head_dim 128, page size 16, kv_len uniform in
+[512, 4096], pages drawn from a 40000-page pool.  Its metric is KV bytes read
+per second.  The other workloads (long-context split-KV decode, causal ragged
+prefill, mixed step with a sliding window) are measured briefly and reported
+under "secondary".
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, published
+
+METRIC = "decode KV-read GB/s (% HBM peak); prefill TFLOP/s (% bf16 MFMA peak)"
+
+DESCR = {
+    "tiny_decode": "tiny decode: 4 requests, Hq 4 / Hk 2, D 64, page 16, kv_len U[1,100]",
+    "gqa_decode": "batched GQA decode + append: 128 requests, Hq 32 / Hk 8, D 128, page 16, "
+                  "kv_len U[512,4096], 40000-page pool",
+    "long_decode": "long-context split-KV decode: 8 requests, Hq 32 / Hk 8, D 128, page 16, "
+                   "kv_len U[32768,131072]",
+    "ragged_prefill": "causal ragged prefill: 16 requests, q_len U[128,2048], prefix U[0,4096], "
+                      "Hq 32 / Hk 8, D 128, page 16",
+    "mixed_window": "mixed step, window 4096: 256 decode rows (kv_len U[256,8192]) + 4 prompt rows "
+                    "(1024 on 2048 prefix), Hq 16 / Hk 16, D 64, page 32",
+}
+
+
+def visible_counts(w):
+    """Per query token: number of visible keys (causal, window), in q order."""
+    out = np.zeros(w.total_q, dtype=np.int64)
+    for r in range(w.batch):
+        n, L = int(w.kv_len[r]), int(w.q_len[r])
+        q0 = int(w.qo_indptr[r])
+        for t in range(L):
+            p = n - L + t
+            hi = p if w.causal else n - 1
+            lo = 0 if w.window_left < 0 else max(0, p - w.window_left)
+            out[q0 + t] = hi - lo + 1
+    return out
+
+
+def work_of(w):
+    """Algorithmic work.  Decode rows (one query): bytes of visible K and V once
+    per KV head, plus q and out.  Prompt rows: 4*D FLOP per visible
+    (query token, query head, key)."""
+    vis = visible_counts(w)
+    is_dec = np.zeros(w.total_q, dtype=bool)
+    for r in range(w.batch):
+        if w.kind == "decode" or (w.kind == "mixed" and w.q_len[r] == 1):
+            is_dec[int(w.qo_indptr[r])] = True
+    D, Hq, Hk = w.head_dim, w.num_qo_heads, w.num_kv_heads
+    kv_bytes = int(vis[is_dec].sum()) * Hk * D * 2 * 2
+    qo_bytes = int(is_dec.sum()) * Hq * D * 2 * 2
+    flops = int(vis[~is_dec].sum()) * Hq * 4 * D
+    return {"kv_bytes": kv_bytes, "decode_bytes": kv_bytes + qo_bytes, "prefill_flops": flops}
+
+
+class Runner:
+    """Holds the device buffers and the plan for one workload."""
+
+    def __init__(self, name, dev):
+        import torch
+        import synth
+        from paged_kv_attention_plan_amd import pkv
+        self.torch, self.pkv = torch, pkv
+        self.name = name
+        self.w = synth.make_workload(name, device=dev)
+        w = self.w
+        if w.k_new is None and w.kind == "decode":
+            g = torch.Generator(device=dev).manual_seed(7)
+            shape = (w.total_q, w.num_kv_heads, w.head_dim)
+            w.k_new = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+            w.v_new = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+        self.qo = None if w.kind == "decode" else w.qo_indptr
+        self.params = pkv.plan_params(w.kind, num_qo_heads=w.num_qo_heads,
+                                      num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                                      page_size=w.page_size, max_pages=w.max_pages,
+                                      causal=w.causal, window_left=w.window_left,
+                                      max_prefill_rows=w.max_prefill_rows)
+        self.plan = pkv.plan_create(self.params, self.qo, w.kv_indptr, w.kv_indices,
+                                    w.last_page_len)
+        self.ws = torch.empty(self.plan.ws_bytes, dtype=torch.uint8, device=dev)
+        self.out = torch.empty_like(w.q)
+        self.lse = torch.empty(w.total_q, w.num_qo_heads, dtype=torch.float32, device=dev)
+        self.append = w.kind == "decode" and name == "gqa_decode"
+        self.work = work_of(w)
+
+    def step(self):
+        w, pkv = self.w, self.pkv
+        pkv.plan_update(self.plan, self.qo, w.kv_indptr, w.kv_indices, w.last_page_len)
+        pkv.plan_upload(self.plan, self.ws)
+        if self.append:
+            pkv.append_kv(self.plan, w.k_new, w.v_new, w.cache, self.ws)
+        pkv.run(self.plan, w.q, w.cache, self.out, self.ws, lse=self.lse)
+
+    def time_steps(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            self.step()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
+
+    def kernel_times(self, steps):
+        """Average per-launch ms of each kernel kind over `steps` steps, from HIP
+        events the library records around its launches on this stream."""
+        pkv = self.pkv
+        pkv.timing_read(self.plan)  # clear
+        pkv.timing_enable(self.plan, True)
+        for _ in range(steps):
+            self.step()
+        res = pkv.timing_read(self.plan)
+        pkv.timing_enable(self.plan, False)
+        return {k: (ms / n if n else None, n) for k, (ms, n) in res.items()}
+
+
+def cpu_baseline(runner, budget_s=12.0):
+    """The oracle, timed on the host on the first rows of the same inputs until
+    about budget_s seconds of work; returns the same unit as the metric."""
+    import torch
+    import oracle
+    w = runner.w
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = max(blas) if blas else 1
+    except Exception:
+        cores = 1
+    done, kv_bytes, flops, elapsed = 0, 0, 0, 0.0
+    for r in range(w.batch):
+        pages = w.kv_indices[w.kv_indptr[r]:w.kv_indptr[r + 1]]
+        sub = w.cache[torch.from_numpy(pages.astype(np.int64)).to(w.cache.device)].cpu()
+        q0, q1 = int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])
+        sub_q = w.q[q0:q1].cpu()
+        t0 = time.perf_counter()
+        oracle.attention_rows(sub_q, sub, w.page_size, np.array([0, len(pages)]),
+                              np.arange(len(pages)), w.last_page_len[r:r + 1],
+                              num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                              qo_indptr=np.array([0, q1 - q0]), causal=w.causal,
+                              window_left=w.window_left)
+        elapsed += time.perf_counter() - t0
+        n = int(w.kv_len[r])
+        kv_bytes += n * w.num_kv_heads * w.head_dim * 4
+        done += 1
+        if elapsed >= budget_s:
+            break
+    return {"value": round(kv_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"first {done} of {w.batch} requests of the same seeded input, every query "
+                      f"head (float64 numpy), {elapsed:.1f} s"}
+
+
+def secondary(name, dev, steps, warmup):
+    r = Runner(name, dev)
+    ms, _ = r.time_steps(steps, warmup)
+    kt = r.kernel_times(steps)
+    res = {"workload": DESCR[name], "ms_per_step": round(ms, 4)}
+    if r.work["kv_bytes"]:
+        dms = kt["decode"][0]
+        res["decode_kernel_us"] = round(dms * 1e3, 2)
+        res["decode_kv_GBps_per_kernel"] = round(r.work["decode_bytes"] / (dms * 1e-3) / 1e9, 1)
+        res["decode_frac_hbm_peak"] = round(res["decode_kv_GBps_per_kernel"] / HBM_PEAK_GBS, 4)
+        if kt["merge"][0] is not None:
+            res["merge_kernel_us"] = round(kt["merge"][0] * 1e3, 2)
+        res["kv_GBps_per_step"] = round(r.work["kv_bytes"] / (ms * 1e-3) / 1e9, 1)
+    if r.work["prefill_flops"]:
+        pms = kt["prefill"][0]
+        res["prefill_kernel_us"] = round(pms * 1e3, 2)
+        res["prefill_TFLOPs_per_kernel"] = round(r.work["prefill_flops"] / (pms * 1e-3) / 1e12, 1)
+        res["prefill_frac_mfma_peak"] = round(res["prefill_TFLOPs_per_kernel"] / MFMA_BF16_PEAK_TFS, 4)
+    del r
+    import torch
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="gqa_decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU code "
+              "(see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_attention_plan_amd import pkv  # noqa: F401  (fails loudly if not built)
+    dev = torch.device("cuda:0")
+
+    r = Runner(args.config, dev)
+    ms, wall_ms = r.time_steps(args.steps, args.warmup)
+    kt = r.kernel_times(args.steps)
+    w = r.work
+    value = w["kv_bytes"] / (ms * 1e-3) / 1e9
+    dec_ms = kt["decode"][0]
+    achieved = w["decode_bytes"] / (dec_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": DESCR[args.config], "kv_bytes_per_step": w["kv_bytes"],
+                   "step": "plan_update + upload + append_kv + run (decode + split-KV merge)"
+                   if r.append else "plan_update + upload + run"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel", "kernel_us": round(dec_ms * 1e3, 2),
+                     "bytes_per_launch": w["decode_bytes"]},
+        "kernels_us": {k: (round(v[0] * 1e3, 2) if v[0] is not None else None)
+                       for k, v in kt.items()},
+        "host_ms_per_step": round(wall_ms, 4),
+    }
+    if not args.no_secondary:
+        sec = []
+        for name in ("long_decode", "ragged_prefill", "mixed_window"):
+            if name != args.config:
+                sec.append(secondary(name, dev, max(5, args.steps // 5), 2))
+        line["secondary"] = sec
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(r)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

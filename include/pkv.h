@@ -203,6 +203,16 @@ pkv_status pkv_append_kv(const pkv_plan* plan, const void* k_new, const void* v_
                          void* kv_cache_layer, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* Per-launch timing, a tracing aid (the wrappers' enable_nvtx flag is the pages'
+ * counterpart).  While enabled, pkv_run and pkv_append_kv record a HIP event on the
+ * stream before and after every kernel they launch with this plan.
+ * pkv_timing_read waits for those events, returns for each kernel kind
+ * ([0] append, [1] decode, [2] split-KV merge, [3] prefill) the summed milliseconds
+ * and the number of launches since the last read, and clears the record.
+ * Events come from a pool the plan owns (created on first use, reused after a read). */
+pkv_status pkv_timing_enable(pkv_plan* plan, int32_t enable);
+pkv_status pkv_timing_read(pkv_plan* plan, double ms[4], int64_t launches[4]);
+
 /* Message for the calling thread's last failed call ("" if none). */
 const char* pkv_last_error(void);
 

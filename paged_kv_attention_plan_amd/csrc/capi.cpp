@@ -1,0 +1,407 @@
+// The C ABI declared in include/pkv.h: plan handles, the pinned staging ring,
+// upload, run and append.  Argument checks happen here, before any launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "pkv.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+pkv_status fail(pkv_status s, std::string msg) {
+  g_err = std::move(msg);
+  return s;
+}
+
+#define PKV_HIP(expr)                                                                    \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return fail(PKV_E_DEVICE, std::string(#expr) + " failed: " + hipGetErrorString(e_)); \
+  } while (0)
+
+// One page-locked host buffer of the staging ring (kv.plan PinnedIndexRing):
+// rewritten only after the copy that last read it has completed.
+struct Stage {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+// Event pairs recorded around launches while timing is enabled.
+struct Timing {
+  bool enabled = false;
+  std::vector<hipEvent_t> pool;  // created lazily, reused after a read
+  size_t used = 0;
+  std::vector<int> kind;         // kernel kind of pair i (events 2i, 2i+1)
+};
+
+struct pkv_plan {
+  pkv::PlanData d;
+  Stage stage[2];
+  int next = 0;
+  void* uploaded_ws = nullptr;
+  mutable Timing timing;
+};
+
+namespace {
+
+enum { kAppend = 0, kDecode = 1, kMerge = 2, kPrefill = 3 };
+
+// Record an event on `s` if timing is on; returns the event (or null).
+hipError_t timing_mark(const pkv_plan* p, hipStream_t s, int kind, bool begin) {
+  Timing& t = p->timing;
+  if (!t.enabled) return hipSuccess;
+  if (begin) {
+    if (t.used + 2 > t.pool.size()) {
+      for (int i = 0; i < 2; ++i) {
+        hipEvent_t e = nullptr;
+        hipError_t err = hipEventCreate(&e);
+        if (err != hipSuccess) return err;
+        t.pool.push_back(e);
+      }
+    }
+    t.kind.push_back(kind);
+    return hipEventRecord(t.pool[t.used], s);
+  }
+  hipError_t err = hipEventRecord(t.pool[t.used + 1], s);
+  t.used += 2;
+  return err;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err.c_str(); }
+
+const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
+
+void pkv_plan_params_init(pkv_plan_params* p) {
+  if (p == nullptr) return;
+  std::memset(p, 0, sizeof(*p));
+  p->kind = PKV_KIND_DECODE;
+  p->causal = 1;
+  p->window_left = -1;
+  p->dtype = PKV_DTYPE_BF16;
+}
+
+static pkv_status resolve_cus(const pkv_plan_params* p, int32_t* cus) {
+  if (p->num_cus > 0) {
+    *cus = p->num_cus;
+    return PKV_OK;
+  }
+  int dev = 0, n = 0;
+  PKV_HIP(hipGetDevice(&dev));
+  PKV_HIP(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev));
+  *cus = n;
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_create(const pkv_plan_params* params, int32_t batch, const int32_t* qo_indptr,
+                           const int32_t* paged_kv_indptr, const int32_t* paged_kv_indices,
+                           const int32_t* paged_kv_last_page_len, const int32_t* kv_lens,
+                           pkv_plan** out, size_t* workspace_bytes) {
+  g_err.clear();
+  if (params == nullptr || out == nullptr || workspace_bytes == nullptr)
+    return fail(PKV_E_INVALID, "params, out and workspace_bytes must not be NULL");
+  *out = nullptr;
+  std::string err;
+  pkv_status st = pkv::check_params(*params, err);
+  if (st != PKV_OK) return fail(st, err);
+  int32_t cus = 0;
+  st = resolve_cus(params, &cus);
+  if (st != PKV_OK) return st;
+  pkv_plan* p = new (std::nothrow) pkv_plan;
+  if (p == nullptr) return fail(PKV_E_INVALID, "out of host memory");
+  st = pkv::build_plan(*params, cus, batch, qo_indptr, paged_kv_indptr, paged_kv_indices,
+                       paged_kv_last_page_len, kv_lens, p->d, err);
+  if (st != PKV_OK) {
+    delete p;
+    return fail(st, err);
+  }
+  *workspace_bytes = p->d.ws.total_bytes;
+  *out = p;
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_update(pkv_plan* plan, int32_t batch, const int32_t* qo_indptr,
+                           const int32_t* paged_kv_indptr, const int32_t* paged_kv_indices,
+                           const int32_t* paged_kv_last_page_len, const int32_t* kv_lens,
+                           size_t* workspace_bytes) {
+  g_err.clear();
+  if (plan == nullptr || workspace_bytes == nullptr)
+    return fail(PKV_E_INVALID, "plan and workspace_bytes must not be NULL");
+  pkv::PlanData fresh;
+  std::string err;
+  pkv_status st = pkv::build_plan(plan->d.params, plan->d.num_cus, batch, qo_indptr,
+                                  paged_kv_indptr, paged_kv_indices, paged_kv_last_page_len,
+                                  kv_lens, fresh, err);
+  if (st != PKV_OK) return fail(st, err);
+  plan->d = std::move(fresh);
+  plan->uploaded_ws = nullptr;
+  *workspace_bytes = plan->d.ws.total_bytes;
+  return PKV_OK;
+}
+
+void pkv_plan_destroy(pkv_plan* plan) {
+  if (plan == nullptr) return;
+  for (hipEvent_t e : plan->timing.pool) (void)hipEventDestroy(e);
+  for (Stage& s : plan->stage) {
+    if (s.pending && s.ev != nullptr) (void)hipEventSynchronize(s.ev);
+    if (s.host != nullptr) (void)hipHostFree(s.host);
+    if (s.ev != nullptr) (void)hipEventDestroy(s.ev);
+  }
+  delete plan;
+}
+
+pkv_status pkv_plan_decode_tiles(const pkv_plan* plan, const pkv_decode_tile** tiles, int32_t* n) {
+  if (plan == nullptr || tiles == nullptr || n == nullptr) return fail(PKV_E_INVALID, "NULL argument");
+  *tiles = plan->d.decode_tiles.data();
+  *n = (int32_t)plan->d.decode_tiles.size();
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_prefill_tiles(const pkv_plan* plan, const pkv_prefill_tile** tiles, int32_t* n) {
+  if (plan == nullptr || tiles == nullptr || n == nullptr) return fail(PKV_E_INVALID, "NULL argument");
+  *tiles = plan->d.prefill_tiles.data();
+  *n = (int32_t)plan->d.prefill_tiles.size();
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_merges(const pkv_plan* plan, const pkv_merge_entry** merges, int32_t* n) {
+  if (plan == nullptr || merges == nullptr || n == nullptr) return fail(PKV_E_INVALID, "NULL argument");
+  *merges = plan->d.merges.data();
+  *n = (int32_t)plan->d.merges.size();
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_write_slots(const pkv_plan* plan, const int64_t** slots, int32_t* n) {
+  if (plan == nullptr || slots == nullptr || n == nullptr) return fail(PKV_E_INVALID, "NULL argument");
+  *slots = plan->d.slots.data();
+  *n = (int32_t)plan->d.slots.size();
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_permutation(const pkv_plan* plan, const int32_t** perm, int32_t* n) {
+  if (plan == nullptr || perm == nullptr || n == nullptr) return fail(PKV_E_INVALID, "NULL argument");
+  *perm = plan->d.perm.data();
+  *n = (int32_t)plan->d.perm.size();
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_info(const pkv_plan* plan, int64_t info[16]) {
+  if (plan == nullptr || info == nullptr) return fail(PKV_E_INVALID, "NULL argument");
+  const pkv::PlanData& d = plan->d;
+  for (int i = 0; i < 16; ++i) info[i] = 0;
+  info[0] = d.total_q;
+  info[1] = d.batch;
+  info[2] = d.n_decode_rows;
+  info[3] = d.n_prompt_rows;
+  info[4] = d.chunk_pages;
+  info[5] = d.n_slots;
+  info[6] = (int64_t)d.ws.meta_bytes;
+  info[7] = (int64_t)d.ws.total_bytes;
+  info[8] = d.num_cus;
+  return PKV_OK;
+}
+
+static pkv_status check_workspace(const pkv_plan* plan, const void* ws, size_t ws_bytes) {
+  const size_t need = plan->d.ws.total_bytes;
+  if (ws == nullptr) return fail(PKV_E_INVALID, "workspace must not be NULL");
+  if (ws_bytes < need)
+    return fail(PKV_E_WORKSPACE,
+                "workspace holds " + std::to_string(ws_bytes) + " bytes; this plan needs " +
+                    std::to_string(need) + " (plan metadata " + std::to_string(plan->d.ws.meta_bytes) +
+                    " + split-KV partials " + std::to_string(need - plan->d.ws.meta_bytes) +
+                    "); pass a workspace of at least workspace_bytes");
+  return PKV_OK;
+}
+
+pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (plan == nullptr) return fail(PKV_E_INVALID, "plan must not be NULL");
+  pkv_status st = check_workspace(plan, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  const size_t meta = plan->d.ws.meta_bytes;
+  Stage& s = plan->stage[plan->next];
+  if (s.pending) {
+    PKV_HIP(hipEventSynchronize(s.ev));
+    s.pending = false;
+  }
+  if (s.cap < meta) {
+    if (s.host != nullptr) PKV_HIP(hipHostFree(s.host));
+    s.host = nullptr;
+    s.cap = 0;
+    size_t cap = 4096;
+    while (cap < meta) cap <<= 1;
+    PKV_HIP(hipHostMalloc(&s.host, cap, hipHostMallocDefault));
+    s.cap = cap;
+  }
+  if (s.ev == nullptr) PKV_HIP(hipEventCreateWithFlags(&s.ev, hipEventDisableTiming));
+  pkv::serialize_meta(plan->d, s.host);
+  hipStream_t st_ = static_cast<hipStream_t>(stream);
+  PKV_HIP(hipMemcpyAsync(workspace, s.host, meta, hipMemcpyHostToDevice, st_));
+  PKV_HIP(hipEventRecord(s.ev, st_));
+  s.pending = true;
+  plan->next ^= 1;
+  plan->uploaded_ws = workspace;
+  return PKV_OK;
+}
+
+pkv_status pkv_run(const pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
+                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (plan == nullptr) return fail(PKV_E_INVALID, "plan must not be NULL");
+  pkv_status st = check_workspace(plan, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  if (plan->uploaded_ws != workspace)
+    return fail(PKV_E_STATE, "the plan was not uploaded to this workspace (call pkv_plan_upload first)");
+  const pkv::PlanData& d = plan->d;
+  if (d.total_q == 0) return PKV_OK;
+  if (q == nullptr || kv_cache_layer == nullptr || out == nullptr)
+    return fail(PKV_E_INVALID, "q, kv_cache_layer and out must not be NULL");
+  if (!aligned16(q) || !aligned16(kv_cache_layer) || !aligned16(out) || !aligned16(workspace))
+    return fail(PKV_E_INVALID, "q, kv_cache_layer, out and workspace must be 16-byte aligned");
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return fail(PKV_E_INVALID, "lse must be 4-byte aligned");
+  const pkv_plan_params& P = d.params;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.head_dim));
+  const int32_t* indices = reinterpret_cast<const int32_t*>(ws + d.ws.off_indices);
+  float* part_o = reinterpret_cast<float*>(ws + d.ws.off_part_o);
+  float* part_lse = reinterpret_cast<float*>(ws + d.ws.off_part_lse);
+  if (!d.decode_tiles.empty()) {
+    pkv::DecodeArgs a{};
+    a.tiles = reinterpret_cast<const pkv_decode_tile*>(ws + d.ws.off_decode_tiles);
+    a.n_tiles = (int32_t)d.decode_tiles.size();
+    a.indices = indices;
+    a.q = static_cast<const uint16_t*>(q);
+    a.cache = static_cast<const uint16_t*>(kv_cache_layer);
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.part_o = part_o;
+    a.part_lse = part_lse;
+    a.num_qo_heads = P.num_qo_heads;
+    a.num_kv_heads = P.num_kv_heads;
+    a.head_dim = P.head_dim;
+    a.page_size = P.page_size;
+    a.group = d.group;
+    a.scale_log2 = scale_log2;
+    PKV_HIP(timing_mark(plan, s, kDecode, true));
+    PKV_HIP(pkv::launch_decode(a, s));
+    PKV_HIP(timing_mark(plan, s, kDecode, false));
+  }
+  if (!d.merges.empty()) {
+    pkv::MergeArgs a{};
+    a.merges = reinterpret_cast<const pkv_merge_entry*>(ws + d.ws.off_merges);
+    a.n_merges = (int32_t)d.merges.size();
+    a.part_o = part_o;
+    a.part_lse = part_lse;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.num_qo_heads = P.num_qo_heads;
+    a.head_dim = P.head_dim;
+    a.group = d.group;
+    PKV_HIP(timing_mark(plan, s, kMerge, true));
+    PKV_HIP(pkv::launch_merge(a, s));
+    PKV_HIP(timing_mark(plan, s, kMerge, false));
+  }
+  if (!d.prefill_tiles.empty()) {
+    pkv::PrefillArgs a{};
+    a.tiles = reinterpret_cast<const pkv_prefill_tile*>(ws + d.ws.off_prefill_tiles);
+    a.n_tiles = (int32_t)d.prefill_tiles.size();
+    a.indices = indices;
+    a.q = static_cast<const uint16_t*>(q);
+    a.cache = static_cast<const uint16_t*>(kv_cache_layer);
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.num_qo_heads = P.num_qo_heads;
+    a.num_kv_heads = P.num_kv_heads;
+    a.head_dim = P.head_dim;
+    a.page_size = P.page_size;
+    a.group = d.group;
+    a.causal = P.causal ? 1 : 0;
+    a.window_left = P.window_left;
+    a.scale_log2 = scale_log2;
+    PKV_HIP(timing_mark(plan, s, kPrefill, true));
+    PKV_HIP(pkv::launch_prefill(a, s));
+    PKV_HIP(timing_mark(plan, s, kPrefill, false));
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_append_kv(const pkv_plan* plan, const void* k_new, const void* v_new,
+                         void* kv_cache_layer, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  g_err.clear();
+  if (plan == nullptr) return fail(PKV_E_INVALID, "plan must not be NULL");
+  pkv_status st = check_workspace(plan, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  if (plan->uploaded_ws != workspace)
+    return fail(PKV_E_STATE, "the plan was not uploaded to this workspace (call pkv_plan_upload first)");
+  const pkv::PlanData& d = plan->d;
+  if (d.total_q == 0) return PKV_OK;
+  if (k_new == nullptr || v_new == nullptr || kv_cache_layer == nullptr)
+    return fail(PKV_E_INVALID, "k_new, v_new and kv_cache_layer must not be NULL");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(kv_cache_layer))
+    return fail(PKV_E_INVALID, "k_new, v_new and kv_cache_layer must be 16-byte aligned");
+  pkv::AppendArgs a{};
+  a.slots = reinterpret_cast<const int64_t*>(static_cast<char*>(workspace) + d.ws.off_slots);
+  a.n_tokens = d.total_q;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.cache = static_cast<uint16_t*>(kv_cache_layer);
+  a.num_kv_heads = d.params.num_kv_heads;
+  a.head_dim = d.params.head_dim;
+  a.page_size = d.params.page_size;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PKV_HIP(timing_mark(plan, s, kAppend, true));
+  PKV_HIP(pkv::launch_append(a, s));
+  PKV_HIP(timing_mark(plan, s, kAppend, false));
+  return PKV_OK;
+}
+
+pkv_status pkv_timing_enable(pkv_plan* plan, int32_t enable) {
+  g_err.clear();
+  if (plan == nullptr) return fail(PKV_E_INVALID, "plan must not be NULL");
+  plan->timing.enabled = enable != 0;
+  return PKV_OK;
+}
+
+pkv_status pkv_timing_read(pkv_plan* plan, double ms[4], int64_t launches[4]) {
+  g_err.clear();
+  if (plan == nullptr || ms == nullptr || launches == nullptr)
+    return fail(PKV_E_INVALID, "NULL argument");
+  for (int i = 0; i < 4; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  Timing& t = plan->timing;
+  for (size_t i = 0; i < t.used / 2; ++i) {
+    PKV_HIP(hipEventSynchronize(t.pool[2 * i + 1]));
+    float e = 0.f;
+    PKV_HIP(hipEventElapsedTime(&e, t.pool[2 * i], t.pool[2 * i + 1]));
+    ms[t.kind[i]] += e;
+    launches[t.kind[i]] += 1;
+  }
+  t.used = 0;
+  t.kind.clear();
+  return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,263 @@
+// Batched GQA decode over a paged KV cache (FlashInferDecodeWrapper.run on the
+// mstar attn.wrappers page; split-KV partials in the workspace, attn.workspace).
+//
+// One wavefront per tile = (row, KV head, contiguous key chunk).  A key row of
+// one KV head is head_dim bf16 = D*2 bytes, contiguous in the cache; it is
+// spread over LPK = D/8 lanes, 16 bytes each, so one wave-wide load fetches
+// KPL = 64/LPK whole key rows with fully used 16-byte lane accesses.  An
+// iteration issues U such loads for K and U for V (KB = KPL*U keys) and the
+// next iteration's loads go out before the current one is computed.
+//
+// Scores: each lane forms the partial dot product of its 8 dimensions with the
+// group's G query heads (bf16 dot2), then a DPP allreduce over its LPK lanes.
+// Softmax: the KPL lane groups of a wave each keep their own running max, sum
+// and output accumulator (fp32, in registers) over the keys they see; the
+// groups are combined once, at the end of the tile, by log-sum-exp.
+//
+// Memory traffic is one read of every visible K and V byte: the kernel is
+// bound by HBM bandwidth.
+#include "common.cuh"
+#include "kernels.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;  // wavefronts (tiles) per workgroup
+
+template <int D, int G, bool ONE_PAGE_PER_ITER>
+__global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
+  constexpr int LPK = D / 8;       // lanes per key row
+  constexpr int KPL = 64 / LPK;    // key rows per wave load
+  constexpr int U = 4;             // loads per iteration (each for K and V)
+  constexpr int KB = KPL * U;      // keys per iteration
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tix = blockIdx.x * kWaves + wave;
+  if (tix >= a.n_tiles) return;
+
+  const pkv_decode_tile* tp = a.tiles + tix;
+  const int hk = __builtin_amdgcn_readfirstlane(tp->kv_head);
+  const int ks = __builtin_amdgcn_readfirstlane(tp->kv_start);
+  const int ke = __builtin_amdgcn_readfirstlane(tp->kv_end);
+  const int page_base = __builtin_amdgcn_readfirstlane(tp->page_base);
+  const int q_index = __builtin_amdgcn_readfirstlane(tp->q_index);
+  const int out_slot = __builtin_amdgcn_readfirstlane(tp->out_slot);
+
+  const int Hq = a.num_qo_heads;
+  const int Hk = a.num_kv_heads;
+  const int ps = a.page_size;
+  const int ps_log2 = __builtin_ctz(ps);
+  const int row_elems = Hk * D;                      // one token slot, all KV heads
+  const int64_t page_elems = 2LL * ps * row_elems;   // K half + V half
+  const int v_off = ps * row_elems;
+
+  const int lk = lane / LPK;   // key row within a load
+  const int ld = lane % LPK;   // 8-element segment of head_dim
+  const int lane_off = hk * D + ld * 8;
+
+  // Query heads hk*G .. hk*G+G-1, this lane's 8 dimensions, as packed bf16 pairs.
+  uint32_t qw[G][4];
+  {
+    const uint16_t* qp = a.q + ((int64_t)q_index * Hq + hk * G) * D + ld * 8;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qp + h * D);
+      qw[h][0] = v.x; qw[h][1] = v.y; qw[h][2] = v.z; qw[h][3] = v.w;
+    }
+  }
+
+  float m[G], l[G], o[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -1e30f;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+  }
+
+  const int kb0 = ks & ~(KB - 1);
+  // Physical page ids of the chunk, 64 at a time: lane i holds logical page
+  // win + i of the row.
+  const int last_lp = (ke - 1) >> ps_log2;
+  int win = kb0 >> ps_log2;
+  int pid_vec = 0;
+  {
+    const int i = win + lane;
+    pid_vec = i <= last_lp ? a.indices[page_base + i] : 0;
+  }
+
+  uint4 kr[U], vr[U];
+  auto issue = [&](int kb, uint4 (&kk)[U], uint4 (&vv)[U]) {
+    if constexpr (ONE_PAGE_PER_ITER) {
+      const int lp = kb >> ps_log2;
+      if (lp - win >= 64) {  // uniform: next window of page ids
+        win += 64;
+        const int i = win + lane;
+        pid_vec = i <= last_lp ? a.indices[page_base + i] : 0;
+      }
+      const int phys = __builtin_amdgcn_readlane(pid_vec, lp - win);
+      const uint16_t* pbase = a.cache + (int64_t)phys * page_elems;
+      const int slot0 = kb & (ps - 1);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int off = (slot0 + u * KPL + lk) * row_elems + lane_off;
+        kk[u] = *reinterpret_cast<const uint4*>(pbase + off);
+        vv[u] = *reinterpret_cast<const uint4*>(pbase + off + v_off);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        int j = kb + u * KPL + lk;
+        j = j < ke ? j : ke - 1;  // keys past the chunk are masked; keep the address valid
+        const int phys = a.indices[page_base + (j >> ps_log2)];
+        const uint16_t* p = a.cache + (int64_t)phys * page_elems +
+                            (j & (ps - 1)) * row_elems + lane_off;
+        kk[u] = *reinterpret_cast<const uint4*>(p);
+        vv[u] = *reinterpret_cast<const uint4*>(p + v_off);
+      }
+    }
+  };
+
+  auto compute = [&](const uint4 (&kk)[U], const uint4 (&vv)[U], int kb) {
+    float s[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float acc = dot2_bf16(qw[h][0], kk[u].x, 0.f);
+        acc = dot2_bf16(qw[h][1], kk[u].y, acc);
+        acc = dot2_bf16(qw[h][2], kk[u].z, acc);
+        acc = dot2_bf16(qw[h][3], kk[u].w, acc);
+        s[u][h] = group_sum<LPK>(acc) * a.scale_log2;
+      }
+    }
+    float vf[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      vf[u][0] = bf16_lo(vv[u].x); vf[u][1] = bf16_hi(vv[u].x);
+      vf[u][2] = bf16_lo(vv[u].y); vf[u][3] = bf16_hi(vv[u].y);
+      vf[u][4] = bf16_lo(vv[u].z); vf[u][5] = bf16_hi(vv[u].z);
+      vf[u][6] = bf16_lo(vv[u].w); vf[u][7] = bf16_hi(vv[u].w);
+    }
+    if (kb < ks || kb + KB > ke) {  // uniform: chunk edges
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = kb + u * KPL + lk;
+        if (j < ks || j >= ke) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) s[u][h] = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vf[u][e] = 0.f;  // stale slots may hold NaN
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mx = s[0][h];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][h]);
+      const float mn = fmaxf(m[h], mx);
+      const float alpha = fast_exp2(m[h] - mn);
+      m[h] = mn;
+      float lsum = l[h] * alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = fast_exp2(s[u][h] - mn);
+        lsum += p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vf[u][e], o[h][e]);
+      }
+      l[h] = lsum;
+    }
+  };
+
+  issue(kb0, kr, vr);
+  for (int kb = kb0; kb < ke; kb += KB) {
+    uint4 kn[U], vn[U];
+    const bool more = kb + KB < ke;
+    if (more) issue(kb + KB, kn, vn);
+    compute(kr, vr, kb);
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) { kr[u] = kn[u]; vr[u] = vn[u]; }
+    }
+  }
+
+  // Combine the KPL lane groups (lanes that differ in bits >= log2(LPK)).
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float M = m[h];
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float sc = fast_exp2(m[h] - M);
+    l[h] *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] *= sc;
+#pragma unroll
+    for (int off = LPK; off < 64; off <<= 1) {
+      l[h] += __shfl_xor(l[h], off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] += __shfl_xor(o[h][e], off);
+    }
+    m[h] = M;
+  }
+
+  if (lk == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float inv = 1.f / l[h];
+      const float lse_nat = (m[h] + log2f(l[h])) * kLn2;
+      const int qh = hk * G + h;
+      if (out_slot < 0) {
+        uint4 pk;
+        pk.x = pack_bf16x2(o[h][0] * inv, o[h][1] * inv);
+        pk.y = pack_bf16x2(o[h][2] * inv, o[h][3] * inv);
+        pk.z = pack_bf16x2(o[h][4] * inv, o[h][5] * inv);
+        pk.w = pack_bf16x2(o[h][6] * inv, o[h][7] * inv);
+        *reinterpret_cast<uint4*>(a.out + ((int64_t)q_index * Hq + qh) * D + ld * 8) = pk;
+        if (a.lse != nullptr && ld == 0) a.lse[(int64_t)q_index * Hq + qh] = lse_nat;
+      } else {
+        float* po = a.part_o + ((int64_t)out_slot * G + h) * D + ld * 8;
+        *reinterpret_cast<float4*>(po) = make_float4(o[h][0] * inv, o[h][1] * inv, o[h][2] * inv, o[h][3] * inv);
+        *reinterpret_cast<float4*>(po + 4) = make_float4(o[h][4] * inv, o[h][5] * inv, o[h][6] * inv, o[h][7] * inv);
+        if (ld == 0) a.part_lse[(int64_t)out_slot * G + h] = lse_nat;
+      }
+    }
+  }
+}
+
+template <int D, int G>
+hipError_t launch_dg(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int KB = (64 / (D / 8)) * 4;
+  const dim3 grid((a.n_tiles + kWaves - 1) / kWaves), block(64 * kWaves);
+  if (a.page_size >= KB)
+    hipLaunchKernelGGL((decode_kernel<D, G, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, G, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.group) {
+    case 1: return launch_dg<D, 1>(a, stream);
+    case 2: return launch_dg<D, 2>(a, stream);
+    case 4: return launch_dg<D, 4>(a, stream);
+    case 8: return launch_dg<D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (a.n_tiles <= 0) return hipSuccess;
+  if (a.head_dim == 128) return launch_d<128>(a, stream);
+  if (a.head_dim == 64) return launch_d<64>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

@@ -1,0 +1,63 @@
+// Launchers for the gfx950 kernels.  Plain pointers only; the C ABI in
+// capi.cpp validates arguments before it calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "pkv.h"
+
+namespace pkv {
+
+struct DecodeArgs {
+  const pkv_decode_tile* tiles;
+  int32_t n_tiles;
+  const int32_t* indices;   // paged_kv_indices on the device
+  const uint16_t* q;        // bf16 [total_q, Hq, D]
+  const uint16_t* cache;    // bf16 [max_pages, 2, ps, Hk, D]
+  uint16_t* out;            // bf16 [total_q, Hq, D]
+  float* lse;               // [total_q, Hq] or null
+  float* part_o;            // [n_slots, group, D]
+  float* part_lse;          // [n_slots, group]
+  int32_t num_qo_heads, num_kv_heads, head_dim, page_size, group;
+  float scale_log2;         // log2(e) / sqrt(head_dim)
+};
+
+struct MergeArgs {
+  const pkv_merge_entry* merges;
+  int32_t n_merges;
+  const float* part_o;
+  const float* part_lse;
+  uint16_t* out;
+  float* lse;
+  int32_t num_qo_heads, head_dim, group;
+};
+
+struct AppendArgs {
+  const int64_t* slots;     // flat page * ps + offset per token
+  int32_t n_tokens;
+  const uint16_t* k_new;    // bf16 [n_tokens, Hk, D]
+  const uint16_t* v_new;
+  uint16_t* cache;
+  int32_t num_kv_heads, head_dim, page_size;
+};
+
+struct PrefillArgs {
+  const pkv_prefill_tile* tiles;
+  int32_t n_tiles;
+  const int32_t* indices;
+  const uint16_t* q;
+  const uint16_t* cache;
+  uint16_t* out;
+  float* lse;
+  int32_t num_qo_heads, num_kv_heads, head_dim, page_size, group;
+  int32_t causal, window_left;
+  float scale_log2;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace pkv

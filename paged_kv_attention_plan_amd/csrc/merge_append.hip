@@ -1,0 +1,94 @@
+// Split-KV merge and KV append.
+//
+// Merge (the workspace page, mstar attn.workspace, keeps split-KV partials):
+// a row whose keys were cut into chunks c has, per query head, a partial output
+// o_c normalised over chunk c alone and its log-sum-exp lse_c.  Over all keys,
+// lse = ln sum_c exp(lse_c) and out = sum_c exp(lse_c - lse) * o_c.
+//
+// Append (FlashInferDecodeWrapper.plan computes the write location; the KV
+// resource stores K/V before attention runs, attn.dense requires_kv_write):
+// token t's K row goes to cache[page, 0, off] and its V row to
+// cache[page, 1, off] with page * page_size + off = slot[t].
+#include "common.cuh"
+#include "kernels.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWaves = 4;
+
+template <int D>
+__global__ __launch_bounds__(64 * kWaves) void merge_kernel(MergeArgs a) {
+  constexpr int E = D / 64;  // elements per lane
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = a.group;
+  const int item = blockIdx.x * kWaves + wave;  // (merge entry, head in group)
+  if (item >= a.n_merges * G) return;
+  const int mi = item / G, h = item - mi * G;
+  const pkv_merge_entry e = a.merges[mi];
+  const float* pl = a.part_lse + (int64_t)e.slot_base * G + h;
+  float M = -INFINITY;
+  for (int c = 0; c < e.n_chunks; ++c) M = fmaxf(M, pl[(int64_t)c * G]);
+  float wsum = 0.f, acc[E];
+#pragma unroll
+  for (int k = 0; k < E; ++k) acc[k] = 0.f;
+  for (int c = 0; c < e.n_chunks; ++c) {
+    const float wc = __expf(pl[(int64_t)c * G] - M);
+    wsum += wc;
+    const float* po = a.part_o + ((int64_t)(e.slot_base + c) * G + h) * D + lane * E;
+#pragma unroll
+    for (int k = 0; k < E; ++k) acc[k] = fmaf(wc, po[k], acc[k]);
+  }
+  const float inv = 1.f / wsum;
+  const int qh = e.kv_head * G + h;
+  uint16_t* dst = a.out + ((int64_t)e.q_index * a.num_qo_heads + qh) * D + lane * E;
+  if constexpr (E == 2) {
+    *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  } else {
+    dst[0] = (uint16_t)bf16_rne(acc[0] * inv);
+  }
+  if (a.lse != nullptr && lane == 0)
+    a.lse[(int64_t)e.q_index * a.num_qo_heads + qh] = M + logf(wsum);
+}
+
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int t = blockIdx.x;
+  const int64_t slot = a.slots[t];
+  const int ps = a.page_size;
+  const int64_t page = slot / ps;
+  const int off = (int)(slot - page * ps);
+  const int row = a.num_kv_heads * a.head_dim;  // elements per token slot
+  const int nvec = row / 8;                     // 16-byte vectors per row
+  uint16_t* dk = a.cache + ((page * 2 + 0) * ps + off) * (int64_t)row;
+  uint16_t* dv = dk + (int64_t)ps * row;
+  const uint4* sk = reinterpret_cast<const uint4*>(a.k_new + (int64_t)t * row);
+  const uint4* sv = reinterpret_cast<const uint4*>(a.v_new + (int64_t)t * row);
+  for (int i = threadIdx.x; i < 2 * nvec; i += blockDim.x) {
+    if (i < nvec) reinterpret_cast<uint4*>(dk)[i] = sk[i];
+    else reinterpret_cast<uint4*>(dv)[i - nvec] = sv[i - nvec];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
+  if (a.n_merges <= 0) return hipSuccess;
+  const int items = a.n_merges * a.group;
+  const dim3 grid((items + kWaves - 1) / kWaves), block(64 * kWaves);
+  if (a.head_dim == 128) hipLaunchKernelGGL(merge_kernel<128>, grid, block, 0, stream, a);
+  else if (a.head_dim == 64) hipLaunchKernelGGL(merge_kernel<64>, grid, block, 0, stream, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
+  if (a.n_tokens <= 0) return hipSuccess;
+  const int nvec2 = 2 * a.num_kv_heads * a.head_dim / 8;
+  int threads = ((nvec2 + 63) / 64) * 64;
+  threads = threads > 256 ? 256 : threads;
+  hipLaunchKernelGGL(append_kernel, dim3(a.n_tokens), dim3(threads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

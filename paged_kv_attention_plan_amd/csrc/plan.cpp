@@ -1,0 +1,373 @@
+// Host planner.  The operations it prepares are documented on the mstar pages:
+//   kv.plan (PagedIndptrs, SequenceView.last_page_len, KVPlanOutput) for the page
+//   table and write locations; attn.wrappers (FlashInferDecodeWrapper.plan,
+//   FlashInferPrefillWrapper.plan, FlashInferMixedWrapper) for the plan inputs,
+//   window_left and the mixed step; attn.workspace (Workspace) for split-KV
+//   partials and a plan size that depends on rows, heads and the CU count.
+//
+// Tiling policy (ours; the pages leave it open):
+//  decode  A row's single query sits at position N-1 and sees keys [lo, N-1],
+//          lo = max(0, N-1-window_left) (or 0).  Its visible pages run from
+//          lo/ps to (N-1)/ps.  The split-KV chunk C (pages) is the smallest
+//          min_chunk_pages * 2^k for which Hk * sum_r ceil(pages_r / C) fits
+//          tiles_per_cu * num_cus, or the first that reaches the longest row.
+//          Rows are taken longest first (ties: lower row index); a row's tiles
+//          are chunk-major, KV-head-minor.  A row cut into n > 1 chunks owns
+//          Hk * n consecutive partial slots (head-major) and one merge per head.
+//  prefill Query tokens are taken in blocks of 128/group so a block fills the
+//          128 rows of a kernel tile; a block's keys are [lo of its first token,
+//          hi of its last token].  Tiles are ordered by key count, largest first
+//          (ties: row, block, KV head), so the longest work is dispatched first.
+#include "plan.h"
+
+#include <algorithm>
+#include <cstring>
+#include <numeric>
+#include <unordered_set>
+
+namespace pkv {
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+std::string fmt_row(const char* what, int64_t r) {
+  return std::string(what) + " (row " + std::to_string(r) + ")";
+}
+
+}  // namespace
+
+pkv_status check_params(const pkv_plan_params& p, std::string& err) {
+  if (p.kind < PKV_KIND_DECODE || p.kind > PKV_KIND_MIXED) {
+    err = "kind must be PKV_KIND_DECODE, PKV_KIND_PREFILL or PKV_KIND_MIXED";
+    return PKV_E_INVALID;
+  }
+  if (p.num_qo_heads < 1 || p.num_kv_heads < 1 || p.num_qo_heads % p.num_kv_heads != 0) {
+    err = "num_qo_heads must be a positive multiple of num_kv_heads (got " +
+          std::to_string(p.num_qo_heads) + ", " + std::to_string(p.num_kv_heads) + ")";
+    return PKV_E_INVALID;
+  }
+  if (p.head_dim != 64 && p.head_dim != 128) {
+    err = "head_dim " + std::to_string(p.head_dim) + " is not computed by this library (64 or 128)";
+    return PKV_E_UNSUPPORTED;
+  }
+  if (p.dtype != PKV_DTYPE_BF16) {
+    err = "only bf16 q/KV are supported";
+    return PKV_E_UNSUPPORTED;
+  }
+  if (!is_pow2(p.page_size) || p.page_size > 256) {
+    err = "page_size must be a power of two in [1, 256] (got " + std::to_string(p.page_size) + ")";
+    return PKV_E_UNSUPPORTED;
+  }
+  if (p.window_left < -1) {
+    err = "window_left must be -1 (unbounded) or >= 0";
+    return PKV_E_INVALID;
+  }
+  if (p.max_pages < 1) {
+    err = "max_pages must be >= 1";
+    return PKV_E_INVALID;
+  }
+  const int g = p.num_qo_heads / p.num_kv_heads;
+  if (p.kind != PKV_KIND_PREFILL && !(g == 1 || g == 2 || g == 4 || g == 8)) {
+    err = "decode rows need num_qo_heads / num_kv_heads in {1, 2, 4, 8} (got " + std::to_string(g) + ")";
+    return PKV_E_UNSUPPORTED;
+  }
+  if (p.kind != PKV_KIND_DECODE && (128 % g) != 0) {
+    err = "prefill rows need num_qo_heads / num_kv_heads to divide 128 (got " + std::to_string(g) + ")";
+    return PKV_E_UNSUPPORTED;
+  }
+  if (p.kind == PKV_KIND_MIXED && p.max_prefill_rows < 0) {
+    err = "max_prefill_rows must be >= 0";
+    return PKV_E_INVALID;
+  }
+  if (p.decode_tiles_per_cu < 0 || p.decode_min_chunk_pages < 0) {
+    err = "tuning knobs must be >= 0 (0 = default)";
+    return PKV_E_INVALID;
+  }
+  return PKV_OK;
+}
+
+pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
+                      const int32_t* qo_indptr, const int32_t* kv_indptr,
+                      const int32_t* kv_indices, const int32_t* last_page_len,
+                      const int32_t* kv_lens, PlanData& out, std::string& err) {
+  pkv_status st = check_params(P, err);
+  if (st != PKV_OK) return st;
+  if (num_cus < 1) {
+    err = "num_cus must be >= 1";
+    return PKV_E_INVALID;
+  }
+  if (batch < 0) {
+    err = "batch must be >= 0";
+    return PKV_E_INVALID;
+  }
+  const bool decode_kind = P.kind == PKV_KIND_DECODE;
+  if (decode_kind && qo_indptr != nullptr) {
+    err = "qo_indptr must be NULL for a decode plan (one query per row)";
+    return PKV_E_INVALID;
+  }
+  if (!decode_kind && qo_indptr == nullptr) {
+    err = "qo_indptr is required for prefill and mixed plans";
+    return PKV_E_INVALID;
+  }
+  if (batch > 0 && (kv_indptr == nullptr || last_page_len == nullptr)) {
+    err = "paged_kv_indptr and paged_kv_last_page_len are required";
+    return PKV_E_INVALID;
+  }
+  const int64_t ps = P.page_size;
+  const int32_t Hk = P.num_kv_heads;
+  const int32_t g = P.num_qo_heads / P.num_kv_heads;
+  const int64_t w = P.window_left;
+
+  // ---- page table: kv.plan PagedIndptrs / SequenceView.last_page_len ----
+  std::vector<int32_t> kv_len(batch), q_len(batch), q_start(batch);
+  if (batch > 0 && kv_indptr[0] != 0) {
+    err = "paged_kv_indptr[0] must be 0";
+    return PKV_E_INVALID;
+  }
+  if (!decode_kind && qo_indptr[0] != 0) {
+    err = "qo_indptr[0] must be 0";
+    return PKV_E_INVALID;
+  }
+  for (int32_t r = 0; r < batch; ++r) {
+    const int64_t np = (int64_t)kv_indptr[r + 1] - kv_indptr[r];
+    if (np < 1) {
+      err = fmt_row("every row needs at least one page", r);
+      return PKV_E_INVALID;
+    }
+    const int64_t lpl = last_page_len[r];
+    if (lpl < 1 || lpl > ps) {
+      err = fmt_row("paged_kv_last_page_len must be in [1, page_size]", r);
+      return PKV_E_INVALID;
+    }
+    const int64_t n = (np - 1) * ps + lpl;
+    if (n > INT32_MAX) {
+      err = fmt_row("kv_len exceeds 2^31-1", r);
+      return PKV_E_INVALID;
+    }
+    kv_len[r] = (int32_t)n;
+    if (kv_lens != nullptr && kv_lens[r] != n) {
+      err = fmt_row("kv_lens disagrees with the page table", r);
+      return PKV_E_INVALID;
+    }
+    int64_t L = 1, qs = r;
+    if (!decode_kind) {
+      L = (int64_t)qo_indptr[r + 1] - qo_indptr[r];
+      qs = qo_indptr[r];
+    }
+    if (L < 0 || L > n) {
+      err = fmt_row("query count must be in [0, kv_len]", r);
+      return PKV_E_INVALID;
+    }
+    q_len[r] = (int32_t)L;
+    q_start[r] = (int32_t)qs;
+  }
+  const int64_t nnz = batch > 0 ? kv_indptr[batch] : 0;
+  if (nnz > 0 && kv_indices == nullptr) {
+    err = "paged_kv_indices is required";
+    return PKV_E_INVALID;
+  }
+  for (int64_t i = 0; i < nnz; ++i) {
+    if (kv_indices[i] < 0 || kv_indices[i] >= P.max_pages) {
+      err = "page id " + std::to_string(kv_indices[i]) + " at index " + std::to_string(i) +
+            " outside [0, max_pages)";
+      return PKV_E_INVALID;
+    }
+  }
+  const int64_t total_q = decode_kind ? batch : (batch > 0 ? qo_indptr[batch] : 0);
+
+  PlanData plan;
+  plan.params = P;
+  plan.batch = batch;
+  plan.total_q = (int32_t)total_q;
+  plan.num_cus = num_cus;
+  plan.group = g;
+  plan.indices.assign(kv_indices, kv_indices + nnz);
+
+  // ---- rows per sub-plan (FlashInferMixedWrapper: one-token rows decode) ----
+  std::vector<int32_t> dec_rows, pre_rows;
+  for (int32_t r = 0; r < batch; ++r) {
+    if (P.kind == PKV_KIND_DECODE) dec_rows.push_back(r);
+    else if (P.kind == PKV_KIND_PREFILL) { if (q_len[r] >= 1) pre_rows.push_back(r); }
+    else if (q_len[r] == 1) dec_rows.push_back(r);
+    else if (q_len[r] >= 2) pre_rows.push_back(r);
+  }
+  if (P.kind == PKV_KIND_MIXED && (int64_t)pre_rows.size() > P.max_prefill_rows) {
+    err = std::to_string(pre_rows.size()) + " prompt rows exceed max_prefill_rows=" +
+          std::to_string(P.max_prefill_rows);
+    return PKV_E_CAPACITY;
+  }
+  plan.n_decode_rows = (int32_t)dec_rows.size();
+  plan.n_prompt_rows = P.kind == PKV_KIND_MIXED ? (int32_t)pre_rows.size() : 0;
+
+  // ---- write slots (FlashInferDecodeWrapper.plan; KVPlanOutput decode_pages/offsets) ----
+  plan.slots.resize(total_q);
+  for (int32_t r = 0; r < batch; ++r) {
+    const int64_t n = kv_len[r], L = q_len[r];
+    for (int64_t t = 0; t < L; ++t) {
+      const int64_t p = n - L + t;
+      const int64_t page = kv_indices[kv_indptr[r] + p / ps];
+      plan.slots[q_start[r] + t] = page * ps + p % ps;
+    }
+  }
+  {
+    std::unordered_set<int64_t> seen;
+    seen.reserve(plan.slots.size() * 2 + 1);
+    for (size_t i = 0; i < plan.slots.size(); ++i) {
+      if (!seen.insert(plan.slots[i]).second) {
+        err = "two appended tokens map to cache slot " + std::to_string(plan.slots[i]) +
+              " (token " + std::to_string(i) + ")";
+        return PKV_E_CONFLICT;
+      }
+    }
+  }
+
+  // ---- mixed permutation: prompt tokens first, rows ascending ----
+  if (P.kind == PKV_KIND_MIXED) {
+    for (int32_t r : pre_rows)
+      for (int32_t t = 0; t < q_len[r]; ++t) plan.perm.push_back(q_start[r] + t);
+  }
+
+  // ---- decode tiles and split-KV chunks ----
+  const int32_t tiles_per_cu = P.decode_tiles_per_cu > 0 ? P.decode_tiles_per_cu : 16;
+  const int32_t min_chunk = P.decode_min_chunk_pages > 0 ? P.decode_min_chunk_pages : 8;
+  struct DecRow { int32_t r; int64_t lo, fp, lp, vis; };
+  std::vector<DecRow> drows;
+  drows.reserve(dec_rows.size());
+  int64_t longest = 0;
+  for (int32_t r : dec_rows) {
+    const int64_t n = kv_len[r];
+    const int64_t lo = w < 0 ? 0 : std::max<int64_t>(0, n - 1 - w);
+    const int64_t fp = lo / ps, lp = (n - 1) / ps;
+    drows.push_back({r, lo, fp, lp, lp - fp + 1});
+    longest = std::max(longest, lp - fp + 1);
+  }
+  int64_t chunk = min_chunk;
+  if (!drows.empty()) {
+    const int64_t budget = (int64_t)tiles_per_cu * num_cus;
+    auto count = [&](int64_t c) {
+      int64_t s = 0;
+      for (auto& d : drows) s += (d.vis + c - 1) / c;
+      return s * Hk;
+    };
+    while (chunk < longest && count(chunk) > budget) chunk *= 2;
+  }
+  plan.chunk_pages = (int32_t)chunk;
+  std::stable_sort(drows.begin(), drows.end(),
+                   [](const DecRow& a, const DecRow& b) { return a.vis > b.vis; });
+  int64_t slot = 0;
+  for (auto& d : drows) {
+    const int64_t n = kv_len[d.r];
+    const int64_t nch = (d.vis + chunk - 1) / chunk;
+    const int64_t base = slot;
+    for (int64_t i = 0; i < nch; ++i) {
+      const int64_t ks = std::max(d.lo, (d.fp + i * chunk) * ps);
+      const int64_t ke = std::min(n, (d.fp + (i + 1) * chunk) * ps);
+      for (int32_t hk = 0; hk < Hk; ++hk) {
+        pkv_decode_tile t;
+        t.row = d.r;
+        t.kv_head = hk;
+        t.kv_start = (int32_t)ks;
+        t.kv_end = (int32_t)ke;
+        t.page_base = kv_indptr[d.r];
+        t.q_index = q_start[d.r];
+        t.out_slot = nch > 1 ? (int32_t)(base + hk * nch + i) : -1;
+        t.kv_len = (int32_t)n;
+        plan.decode_tiles.push_back(t);
+      }
+    }
+    if (nch > 1) {
+      for (int32_t hk = 0; hk < Hk; ++hk)
+        plan.merges.push_back({q_start[d.r], hk, (int32_t)(base + hk * nch), (int32_t)nch});
+      slot += Hk * nch;
+    }
+  }
+  if (slot > INT32_MAX) {
+    err = "too many split-KV partials";
+    return PKV_E_INVALID;
+  }
+  plan.n_slots = (int32_t)slot;
+
+  // ---- prefill tiles ----
+  if (!pre_rows.empty()) {
+    const int64_t bt = 128 / g;
+    struct Item { int64_t keys; int32_t r, b, hk; pkv_prefill_tile t; };
+    std::vector<Item> items;
+    for (int32_t r : pre_rows) {
+      const int64_t n = kv_len[r], L = q_len[r];
+      for (int64_t b = 0; b * bt < L; ++b) {
+        const int64_t qs = b * bt, qc = std::min(bt, L - qs);
+        const int64_t p0 = n - L + qs, p1 = p0 + qc - 1;
+        const int64_t lo = w < 0 ? 0 : std::max<int64_t>(0, p0 - w);
+        const int64_t hi = P.causal ? p1 : n - 1;
+        for (int32_t hk = 0; hk < Hk; ++hk) {
+          pkv_prefill_tile t{};
+          t.row = r;
+          t.kv_head = hk;
+          t.q_start = (int32_t)qs;
+          t.q_count = (int32_t)qc;
+          t.kv_lo = (int32_t)lo;
+          t.kv_hi = (int32_t)hi;
+          t.page_base = kv_indptr[r];
+          t.q_base = q_start[r];
+          t.kv_len = (int32_t)n;
+          t.q_len = (int32_t)L;
+          items.push_back({hi - lo + 1, r, (int32_t)b, hk, t});
+        }
+      }
+    }
+    std::sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
+      if (a.keys != b.keys) return a.keys > b.keys;
+      if (a.r != b.r) return a.r < b.r;
+      if (a.b != b.b) return a.b < b.b;
+      return a.hk < b.hk;
+    });
+    plan.prefill_tiles.reserve(items.size());
+    for (auto& it : items) plan.prefill_tiles.push_back(it.t);
+  }
+
+  // ---- workspace layout ----
+  WorkspaceLayout& L = plan.ws;
+  size_t off = kAlign;  // first 256 bytes reserved
+  L.off_decode_tiles = off;
+  off = align_up(off + plan.decode_tiles.size() * sizeof(pkv_decode_tile));
+  L.off_merges = off;
+  off = align_up(off + plan.merges.size() * sizeof(pkv_merge_entry));
+  L.off_prefill_tiles = off;
+  off = align_up(off + plan.prefill_tiles.size() * sizeof(pkv_prefill_tile));
+  L.off_indices = off;
+  off = align_up(off + plan.indices.size() * sizeof(int32_t));
+  L.off_slots = off;
+  off = align_up(off + plan.slots.size() * sizeof(int64_t));
+  L.meta_bytes = off;
+  L.off_part_o = off;
+  off = align_up(off + (size_t)plan.n_slots * g * P.head_dim * sizeof(float));
+  L.off_part_lse = off;
+  off = align_up(off + (size_t)plan.n_slots * g * sizeof(float));
+  L.total_bytes = off;
+
+  out = std::move(plan);
+  return PKV_OK;
+}
+
+void serialize_meta(const PlanData& plan, void* dst) {
+  char* base = static_cast<char*>(dst);
+  std::memset(base, 0, plan.ws.meta_bytes);
+  const int64_t hdr[8] = {(int64_t)plan.decode_tiles.size(), (int64_t)plan.merges.size(),
+                          (int64_t)plan.prefill_tiles.size(), (int64_t)plan.indices.size(),
+                          (int64_t)plan.slots.size(), plan.n_slots, plan.total_q, plan.batch};
+  std::memcpy(base, hdr, sizeof(hdr));
+  auto put = [&](size_t off, const void* src, size_t bytes) {
+    if (bytes) std::memcpy(base + off, src, bytes);
+  };
+  put(plan.ws.off_decode_tiles, plan.decode_tiles.data(),
+      plan.decode_tiles.size() * sizeof(pkv_decode_tile));
+  put(plan.ws.off_merges, plan.merges.data(), plan.merges.size() * sizeof(pkv_merge_entry));
+  put(plan.ws.off_prefill_tiles, plan.prefill_tiles.data(),
+      plan.prefill_tiles.size() * sizeof(pkv_prefill_tile));
+  put(plan.ws.off_indices, plan.indices.data(), plan.indices.size() * sizeof(int32_t));
+  put(plan.ws.off_slots, plan.slots.data(), plan.slots.size() * sizeof(int64_t));
+}
+
+}  // namespace pkv

@@ -1,0 +1,62 @@
+// Host-side planner for paged-KV attention: page-table validation, work tiles,
+// split-KV chunking, workspace layout, KV write slots and the mixed-step
+// permutation.  No HIP dependency: everything here is plain C++ on the host.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Byte offsets of the regions of a plan's device workspace.  The metadata
+// regions [0, meta_bytes) are filled by the upload; the partial regions are
+// scratch written by split decode tiles and read by the merge.
+struct WorkspaceLayout {
+  size_t off_decode_tiles = 0;
+  size_t off_merges = 0;
+  size_t off_prefill_tiles = 0;
+  size_t off_indices = 0;
+  size_t off_slots = 0;
+  size_t meta_bytes = 0;
+  size_t off_part_o = 0;    // float [n_slots][group][head_dim]
+  size_t off_part_lse = 0;  // float [n_slots][group]
+  size_t total_bytes = 0;
+};
+
+struct PlanData {
+  pkv_plan_params params{};
+  int32_t batch = 0;
+  int32_t total_q = 0;
+  int32_t num_cus = 0;
+  int32_t group = 1;
+  int32_t chunk_pages = 0;
+  int32_t n_slots = 0;
+  int32_t n_decode_rows = 0;
+  int32_t n_prompt_rows = 0;
+  std::vector<pkv_decode_tile> decode_tiles;
+  std::vector<pkv_merge_entry> merges;
+  std::vector<pkv_prefill_tile> prefill_tiles;
+  std::vector<int32_t> indices;  // copy of paged_kv_indices
+  std::vector<int64_t> slots;    // flat write slot per query token
+  std::vector<int32_t> perm;     // mixed: prompt tokens first
+  WorkspaceLayout ws;
+};
+
+// Validate the page table and fill `out`.  num_cus must already be resolved
+// (> 0).  On failure returns the status and sets `err`.
+pkv_status build_plan(const pkv_plan_params& params, int32_t num_cus, int32_t batch,
+                      const int32_t* qo_indptr, const int32_t* kv_indptr,
+                      const int32_t* kv_indices, const int32_t* last_page_len,
+                      const int32_t* kv_lens, PlanData& out, std::string& err);
+
+// Parameter checks that do not need the page table.
+pkv_status check_params(const pkv_plan_params& p, std::string& err);
+
+// Copy the metadata regions of `plan` into `dst` (meta_bytes bytes).
+void serialize_meta(const PlanData& plan, void* dst);
+
+}  // namespace pkv

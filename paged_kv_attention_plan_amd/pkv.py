@@ -1,0 +1,292 @@
+"""ctypes binding of libpkv.so (include/pkv.h), one Python function per C call.
+
+Argument marshalling only: host index arrays become int32 pointers, torch
+device tensors become raw device pointers, the stream is the current HIP
+stream.  Every step of the path runs in the library.  There is no fallback:
+if libpkv.so is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+# ---- status codes and enums (pkv.h) ----
+OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_CAPACITY, E_CONFLICT, E_DEVICE, E_STATE = range(8)
+KIND_DECODE, KIND_PREFILL, KIND_MIXED = 0, 1, 2
+DTYPE_BF16 = 0
+_KINDS = {"decode": KIND_DECODE, "prefill": KIND_PREFILL, "mixed": KIND_MIXED}
+
+STATUS_NAMES = {OK: "PKV_OK", E_INVALID: "PKV_E_INVALID", E_UNSUPPORTED: "PKV_E_UNSUPPORTED",
+                E_WORKSPACE: "PKV_E_WORKSPACE", E_CAPACITY: "PKV_E_CAPACITY",
+                E_CONFLICT: "PKV_E_CONFLICT", E_DEVICE: "PKV_E_DEVICE", E_STATE: "PKV_E_STATE"}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class PlanParams(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("num_qo_heads", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("page_size", C.c_int32), ("causal", C.c_int32),
+                ("window_left", C.c_int32), ("dtype", C.c_int32), ("max_prefill_rows", C.c_int32),
+                ("num_cus", C.c_int32), ("max_pages", C.c_int64),
+                ("decode_tiles_per_cu", C.c_int32), ("decode_min_chunk_pages", C.c_int32)]
+
+
+DECODE_TILE = np.dtype([("row", "<i4"), ("kv_head", "<i4"), ("kv_start", "<i4"), ("kv_end", "<i4"),
+                        ("page_base", "<i4"), ("q_index", "<i4"), ("out_slot", "<i4"),
+                        ("kv_len", "<i4")])
+MERGE_ENTRY = np.dtype([("q_index", "<i4"), ("kv_head", "<i4"), ("slot_base", "<i4"),
+                        ("n_chunks", "<i4")])
+PREFILL_TILE = np.dtype([("row", "<i4"), ("kv_head", "<i4"), ("q_start", "<i4"),
+                         ("q_count", "<i4"), ("kv_lo", "<i4"), ("kv_hi", "<i4"),
+                         ("page_base", "<i4"), ("q_base", "<i4"), ("kv_len", "<i4"),
+                         ("q_len", "<i4"), ("pad0", "<i4"), ("pad1", "<i4")])
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run "
+                           "`python -m paged_kv_attention_plan_amd.build` (ROCm hipcc, gfx950)")
+    lib = C.CDLL(LIB_PATH)
+    P = C.POINTER
+    i32p = P(C.c_int32)
+    sig = {
+        "pkv_plan_params_init": (None, [P(PlanParams)]),
+        "pkv_plan_create": (C.c_int, [P(PlanParams), C.c_int32, i32p, i32p, i32p, i32p, i32p,
+                                      P(C.c_void_p), P(C.c_size_t)]),
+        "pkv_plan_update": (C.c_int, [C.c_void_p, C.c_int32, i32p, i32p, i32p, i32p, i32p,
+                                      P(C.c_size_t)]),
+        "pkv_plan_destroy": (None, [C.c_void_p]),
+        "pkv_plan_decode_tiles": (C.c_int, [C.c_void_p, P(C.c_void_p), P(C.c_int32)]),
+        "pkv_plan_prefill_tiles": (C.c_int, [C.c_void_p, P(C.c_void_p), P(C.c_int32)]),
+        "pkv_plan_merges": (C.c_int, [C.c_void_p, P(C.c_void_p), P(C.c_int32)]),
+        "pkv_plan_write_slots": (C.c_int, [C.c_void_p, P(C.c_void_p), P(C.c_int32)]),
+        "pkv_plan_permutation": (C.c_int, [C.c_void_p, P(C.c_void_p), P(C.c_int32)]),
+        "pkv_plan_info": (C.c_int, [C.c_void_p, P(C.c_int64)]),
+        "pkv_plan_upload": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+        "pkv_run": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                              C.c_void_p, C.c_size_t, C.c_void_p]),
+        "pkv_append_kv": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                    C.c_size_t, C.c_void_p]),
+        "pkv_timing_enable": (C.c_int, [C.c_void_p, C.c_int32]),
+        "pkv_timing_read": (C.c_int, [C.c_void_p, P(C.c_double), P(C.c_int64)]),
+        "pkv_last_error": (C.c_char_p, []),
+        "pkv_version": (C.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("pkv_plan_params_init", "pkv_plan_create", "pkv_plan_update", "pkv_plan_destroy",
+            "pkv_plan_decode_tiles", "pkv_plan_prefill_tiles", "pkv_plan_merges",
+            "pkv_plan_write_slots", "pkv_plan_permutation", "pkv_plan_info", "pkv_plan_upload",
+            "pkv_run", "pkv_append_kv", "pkv_timing_enable", "pkv_timing_read",
+            "pkv_last_error", "pkv_version")
+
+
+def _check(status: int):
+    if status != OK:
+        raise PkvError(status, _lib.pkv_last_error().decode())
+
+
+def _i32(a) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor (host)
+        if a.device.type != "cpu":
+            raise ValueError("plan inputs must be host arrays (pass CPU tensors or numpy arrays)")
+        a = a.detach().numpy()
+    return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return a.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def version() -> str:
+    return _lib.pkv_version().decode()
+
+
+def plan_params(kind="decode", *, num_qo_heads, num_kv_heads, head_dim, page_size, max_pages,
+                causal=True, window_left=-1, max_prefill_rows=0, num_cus=0,
+                decode_tiles_per_cu=0, decode_min_chunk_pages=0) -> PlanParams:
+    p = PlanParams()
+    _lib.pkv_plan_params_init(C.byref(p))
+    p.kind = _KINDS[kind] if isinstance(kind, str) else int(kind)
+    p.num_qo_heads, p.num_kv_heads, p.head_dim, p.page_size = num_qo_heads, num_kv_heads, head_dim, page_size
+    p.causal, p.window_left, p.dtype = int(bool(causal)), int(window_left), DTYPE_BF16
+    p.max_prefill_rows, p.num_cus, p.max_pages = int(max_prefill_rows), int(num_cus), int(max_pages)
+    p.decode_tiles_per_cu, p.decode_min_chunk_pages = int(decode_tiles_per_cu), int(decode_min_chunk_pages)
+    return p
+
+
+class Plan:
+    """Owner of a pkv_plan handle."""
+
+    def __init__(self, handle, ws_bytes: int, params: PlanParams, max_page_id: int = -1):
+        self._h = handle
+        self.ws_bytes = ws_bytes
+        self.params = params
+        self.max_page_id = max_page_id
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and _lib is not None:
+            _lib.pkv_plan_destroy(h)
+
+    def _arr(self, fn, dtype):
+        ptr, n = C.c_void_p(), C.c_int32()
+        _check(fn(self._h, C.byref(ptr), C.byref(n)))
+        if n.value == 0:
+            return np.zeros(0, dtype=dtype)
+        buf = (C.c_char * (n.value * dtype.itemsize)).from_address(ptr.value)
+        return np.frombuffer(buf, dtype=dtype).copy()
+
+    def decode_tiles(self):
+        return self._arr(_lib.pkv_plan_decode_tiles, DECODE_TILE)
+
+    def prefill_tiles(self):
+        return self._arr(_lib.pkv_plan_prefill_tiles, PREFILL_TILE)
+
+    def merges(self):
+        return self._arr(_lib.pkv_plan_merges, MERGE_ENTRY)
+
+    def write_slots(self):
+        return self._arr(_lib.pkv_plan_write_slots, np.dtype("<i8"))
+
+    def permutation(self):
+        return self._arr(_lib.pkv_plan_permutation, np.dtype("<i4"))
+
+    def info(self) -> dict:
+        v = (C.c_int64 * 16)()
+        _check(_lib.pkv_plan_info(self._h, v))
+        keys = ["total_q", "batch", "decode_rows", "prompt_rows", "chunk_pages", "partial_slots",
+                "meta_bytes", "workspace_bytes", "num_cus"]
+        return {k: int(v[i]) for i, k in enumerate(keys)}
+
+
+def plan_create(params: PlanParams, qo_indptr, paged_kv_indptr, paged_kv_indices,
+                paged_kv_last_page_len, kv_lens=None) -> Plan:
+    """pkv_plan_create: validate the page table and build a plan (host only)."""
+    qo, ind, idx, lpl, kvl = map(_i32, (qo_indptr, paged_kv_indptr, paged_kv_indices,
+                                        paged_kv_last_page_len, kv_lens))
+    batch = len(lpl)
+    h, ws = C.c_void_p(), C.c_size_t()
+    _check(_lib.pkv_plan_create(C.byref(params), batch, _ptr(qo), _ptr(ind), _ptr(idx), _ptr(lpl),
+                                _ptr(kvl), C.byref(h), C.byref(ws)))
+    return Plan(h.value, ws.value, params, int(idx.max()) if idx.size else -1)
+
+
+def plan_update(plan: Plan, qo_indptr, paged_kv_indptr, paged_kv_indices, paged_kv_last_page_len,
+                kv_lens=None) -> int:
+    """pkv_plan_update: re-plan the same handle for a new step; returns workspace bytes."""
+    qo, ind, idx, lpl, kvl = map(_i32, (qo_indptr, paged_kv_indptr, paged_kv_indices,
+                                        paged_kv_last_page_len, kv_lens))
+    ws = C.c_size_t()
+    _check(_lib.pkv_plan_update(plan.handle, len(lpl), _ptr(qo), _ptr(ind), _ptr(idx), _ptr(lpl),
+                                _ptr(kvl), C.byref(ws)))
+    plan.ws_bytes = ws.value
+    plan.max_page_id = int(idx.max()) if idx.size else -1
+    return ws.value
+
+
+def _stream(stream):
+    if stream is not None:
+        return C.c_void_p(int(stream))
+    import torch
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return C.c_void_p(t.data_ptr())
+
+
+def plan_upload(plan: Plan, workspace, stream=None):
+    """pkv_plan_upload: async copy of the plan metadata into the workspace head."""
+    _check(_lib.pkv_plan_upload(plan.handle, _dev(workspace, "workspace"),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def _check_sizes(plan: Plan, kv_cache_layer, **tensors):
+    """The C ABI takes raw pointers; make sure the tensors hold what the plan
+    will touch before handing them over."""
+    pp = plan.params
+    T = plan.info()["total_q"]
+    want = {"q": T * pp.num_qo_heads * pp.head_dim, "out": T * pp.num_qo_heads * pp.head_dim,
+            "lse": T * pp.num_qo_heads, "k_new": T * pp.num_kv_heads * pp.head_dim,
+            "v_new": T * pp.num_kv_heads * pp.head_dim}
+    for name, t in tensors.items():
+        if t is not None and t.numel() != want[name]:
+            raise ValueError(f"{name} has {t.numel()} elements; the plan needs {want[name]}")
+    page = 2 * pp.page_size * pp.num_kv_heads * pp.head_dim
+    if kv_cache_layer.numel() % page != 0:
+        raise ValueError("kv_cache_layer is not a whole number of pages")
+    if plan.max_page_id >= kv_cache_layer.numel() // page:
+        raise ValueError(f"the plan reads page {plan.max_page_id}; kv_cache_layer holds "
+                         f"{kv_cache_layer.numel() // page} pages")
+
+
+def run(plan: Plan, q, kv_cache_layer, out, workspace, lse=None, stream=None):
+    """pkv_run: attention for every planned query, written into out (and lse)."""
+    import torch
+    _check_sizes(plan, kv_cache_layer, q=q, out=out, lse=lse)
+    _check(_lib.pkv_run(plan.handle, _dev(q, "q", torch.bfloat16),
+                        _dev(kv_cache_layer, "kv_cache_layer", torch.bfloat16),
+                        _dev(out, "out", torch.bfloat16), _dev(lse, "lse", torch.float32),
+                        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                        _stream(stream)))
+
+
+def append_kv(plan: Plan, k_new, v_new, kv_cache_layer, workspace, stream=None):
+    """pkv_append_kv: store this step's K/V at the planned write slots."""
+    import torch
+    _check_sizes(plan, kv_cache_layer, k_new=k_new, v_new=v_new)
+    _check(_lib.pkv_append_kv(plan.handle, _dev(k_new, "k_new", torch.bfloat16),
+                              _dev(v_new, "v_new", torch.bfloat16),
+                              _dev(kv_cache_layer, "kv_cache_layer", torch.bfloat16),
+                              _dev(workspace, "workspace"),
+                              workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+TIMING_KINDS = ("append", "decode", "merge", "prefill")
+
+
+def timing_enable(plan: Plan, enable: bool = True):
+    """pkv_timing_enable: record HIP events around every launch of this plan."""
+    _check(_lib.pkv_timing_enable(plan.handle, 1 if enable else 0))
+
+
+def timing_read(plan: Plan) -> dict:
+    """pkv_timing_read: {kind: (summed ms, launches)} since the last read."""
+    ms = (C.c_double * 4)()
+    n = (C.c_int64 * 4)()
+    _check(_lib.pkv_timing_read(plan.handle, ms, n))
+    return {k: (float(ms[i]), int(n[i])) for i, k in enumerate(TIMING_KINDS)}

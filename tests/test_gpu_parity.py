@@ -1,0 +1,243 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small cases are compared element by element over every output; the full-size
+workloads are run in the launch configuration the benchmark times and
+compared on sampled rows/tokens.  Tolerances: |out - ref| <= 1e-2 plus half a
+bf16 ulp of ref (the bf16 output's own rounding), max |lse - ref| <= 1e-3;
+write slots and appended bytes bit-exact.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_common import compare, gpu_run, oracle_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv(gpu):
+    from paged_kv_attention_plan_amd import pkv as mod
+    return mod
+
+
+def _full_oracle(w):
+    wc = w.to("cpu")
+    return oracle.attention(wc.q, wc.cache, w.page_size, w.kv_indptr, w.kv_indices,
+                            w.last_page_len, num_qo_heads=w.num_qo_heads,
+                            num_kv_heads=w.num_kv_heads,
+                            qo_indptr=None if w.kind == "decode" else w.qo_indptr,
+                            causal=w.causal, window_left=w.window_left)
+
+
+def test_tiny_decode_matches_golden_and_oracle(pkv, gpu):
+    say("case tiny_decode (4 rows, Hq 4 / Hk 2, D 64, ps 16)")
+    w = synth.make_workload("tiny_decode").to(gpu)
+    out, lse, plan, _ = gpu_run(pkv, w)
+    doc = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "tiny_decode.json")))
+    compare(out, lse, np.array(doc["out"]), np.array(doc["lse"]), "tiny_decode vs golden")
+    ref_o, ref_l = _full_oracle(w)
+    compare(out, lse, ref_o, ref_l, "tiny_decode vs oracle")
+    assert list(plan.write_slots()) == doc["write_slots"]
+
+
+DECODE = [
+    # (seed, head_dim, Hq, Hk, page_size, window, stale, force_split)
+    (100, 64, 4, 2, 16, -1, "nan", False),
+    (101, 128, 32, 8, 16, -1, "nan", True),
+    (102, 128, 8, 8, 1, -1, "nan", True),
+    (103, 64, 16, 2, 64, 37, "nan", True),
+    (104, 128, 16, 16, 32, 0, "nan", False),
+    (105, 64, 8, 4, 4, 100, "zero", True),
+    (106, 128, 16, 2, 256, -1, "nan", True),
+    (107, 64, 2, 1, 8, -1, "nan", True),
+]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: f"s{c[0]}-D{c[1]}-g{c[2]//c[3]}-ps{c[4]}-w{c[5]}")
+def test_decode_small(pkv, gpu, case):
+    seed, D, hq, hk, ps, wl, stale, split = case
+    say(f"case decode seed={seed} D={D} Hq={hq} Hk={hk} ps={ps} window={wl} split={split}")
+    w = synth.random_case(seed, kind="decode", batch=9, num_qo_heads=hq, num_kv_heads=hk,
+                          head_dim=D, page_size=ps, max_kv=700, window_left=wl, stale=stale,
+                          device=gpu)
+    # a large tile budget with 1-page chunks makes the planner cut rows into chunks
+    kw = dict(num_cus=64, decode_tiles_per_cu=16, decode_min_chunk_pages=1) if split else {}
+    out, lse, plan, _ = gpu_run(pkv, w, **kw)
+    if split:
+        assert len(plan.merges()) > 0
+    ref_o, ref_l = _full_oracle(w)
+    compare(out, lse, ref_o, ref_l, f"decode s{seed}")
+
+
+PREFILL = [
+    # (seed, head_dim, Hq, Hk, page_size, causal, window, stale)
+    (200, 128, 32, 8, 16, True, -1, "nan"),
+    (201, 64, 4, 4, 16, True, -1, "nan"),
+    (202, 128, 8, 1, 1, True, 5, "nan"),
+    (203, 64, 16, 2, 32, False, -1, "nan"),
+    (204, 128, 4, 2, 64, False, 40, "nan"),
+    (205, 64, 8, 8, 4, True, 0, "zero"),
+    (206, 128, 16, 16, 16, True, 300, "nan"),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL, ids=lambda c: f"s{c[0]}-D{c[1]}-g{c[2]//c[3]}-ps{c[4]}-c{int(c[5])}-w{c[6]}")
+def test_prefill_small(pkv, gpu, case):
+    seed, D, hq, hk, ps, causal, wl, stale = case
+    say(f"case prefill seed={seed} D={D} Hq={hq} Hk={hk} ps={ps} causal={causal} window={wl}")
+    w = synth.random_case(seed, kind="prefill", batch=6, num_qo_heads=hq, num_kv_heads=hk,
+                          head_dim=D, page_size=ps, max_kv=600, causal=causal, window_left=wl,
+                          stale=stale, device=gpu)
+    out, lse, plan, _ = gpu_run(pkv, w)
+    ref_o, ref_l = _full_oracle(w)
+    compare(out, lse, ref_o, ref_l, f"prefill s{seed}")
+
+
+def test_mixed_small(pkv, gpu):
+    say("case mixed_window cut to 12 decode rows + 4 prompt rows")
+    w = synth.make_workload("mixed_window", scale_rows=12, device=gpu, stale="nan")
+    out, lse, plan, _ = gpu_run(pkv, w)
+    ref_o, ref_l = _full_oracle(w)
+    compare(out, lse, ref_o, ref_l, "mixed small")
+
+
+def test_decode_equals_prefill_one_token(pkv, gpu):
+    say("case decode vs prefill with one query per row")
+    w = synth.random_case(300, kind="decode", batch=7, num_qo_heads=8, num_kv_heads=2,
+                          head_dim=128, page_size=16, max_kv=400, device=gpu)
+    o1, l1, _, _ = gpu_run(pkv, w)
+    o2, l2, _, _ = gpu_run(pkv, w, kind="prefill")
+    assert (o1.float() - o2.float()).abs().max().item() <= 1e-2
+    assert (l1 - l2).abs().max().item() <= 1e-3
+
+
+def test_append_kv_bit_exact(pkv, gpu):
+    say("case append_kv: decode rows, slots at last_page_len - 1")
+    w = synth.random_case(310, kind="decode", batch=11, num_qo_heads=8, num_kv_heads=4,
+                          head_dim=128, page_size=16, max_kv=300, new_tokens=True, device=gpu)
+    before = w.cache.clone()
+    p = pkv.plan_create(pkv.plan_params("decode", num_qo_heads=8, num_kv_heads=4, head_dim=128,
+                                        page_size=16, max_pages=w.max_pages),
+                        None, w.kv_indptr, w.kv_indices, w.last_page_len)
+    ws = torch.empty(p.ws_bytes, dtype=torch.uint8, device=gpu)
+    pkv.plan_upload(p, ws)
+    pkv.append_kv(p, w.k_new, w.v_new, w.cache, ws)
+    torch.cuda.synchronize()
+    slots = oracle.write_slots(16, w.kv_indptr, w.kv_indices, w.last_page_len)
+    assert np.array_equal(p.write_slots(), slots)
+    bits = lambda t: t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    want = oracle.apply_append(bits(before), slots, bits(w.k_new), bits(w.v_new), 16)
+    assert np.array_equal(bits(w.cache), want)
+
+
+def test_append_prefill_tokens_bit_exact(pkv, gpu):
+    say("case append_kv: ragged prefill tokens")
+    w = synth.random_case(311, kind="prefill", batch=5, num_qo_heads=4, num_kv_heads=2,
+                          head_dim=64, page_size=8, max_kv=200, new_tokens=True, device=gpu)
+    before = w.cache.clone()
+    _, _, p, ws = gpu_run(pkv, w, append=True)
+    slots = oracle.write_slots(8, w.kv_indptr, w.kv_indices, w.last_page_len, qo_indptr=w.qo_indptr)
+    bits = lambda t: t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    want = oracle.apply_append(bits(before), slots, bits(w.k_new), bits(w.v_new), 8)
+    assert np.array_equal(bits(w.cache), want)
+
+
+def test_page_relabelling_is_bit_identical(pkv, gpu):
+    say("case page relabelling")
+    w = synth.random_case(320, kind="prefill", batch=5, num_qo_heads=8, num_kv_heads=2,
+                          head_dim=128, page_size=16, max_kv=500, device=gpu, extra_pages=9)
+    o1, l1, _, _ = gpu_run(pkv, w)
+    perm = np.random.default_rng(5).permutation(w.max_pages)
+    cache2 = torch.empty_like(w.cache)
+    cache2[torch.from_numpy(perm).to(gpu)] = w.cache
+    w2 = synth.Workload(**{**w.__dict__, "cache": cache2,
+                           "kv_indices": perm[w.kv_indices].astype(np.int32)})
+    o2, l2, _, _ = gpu_run(pkv, w2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_repeat_runs_are_deterministic(pkv, gpu):
+    say("case repeat determinism (split decode)")
+    w = synth.random_case(330, kind="decode", batch=9, num_qo_heads=32, num_kv_heads=8,
+                          head_dim=128, page_size=16, max_kv=900, device=gpu)
+    kw = dict(num_cus=64, decode_tiles_per_cu=16, decode_min_chunk_pages=1)
+    o1, l1, p1, _ = gpu_run(pkv, w, **kw)
+    o2, l2, _, _ = gpu_run(pkv, w, **kw)
+    assert len(p1.merges()) > 0
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---- full sizes, sampled ----
+
+def _sample_rows(n, k, seed):
+    rng = np.random.default_rng(seed)
+    return sorted(rng.choice(n, size=min(k, n), replace=False).tolist())
+
+
+def test_full_gqa_decode_with_append(pkv, gpu):
+    say("case gqa_decode full size (128 rows, Hq 32 / Hk 8, D 128, ps 16, 40000-page pool) + append")
+    w = synth.make_workload("gqa_decode", device=gpu)
+    out, lse, plan, _ = gpu_run(pkv, w, append=True)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    rows = _sample_rows(w.batch, 10, 1) + [int(np.argmax(w.kv_len))]
+    ref = oracle_rows(w, rows)
+    for r in rows:
+        compare(out[r:r + 1], lse[r:r + 1], ref[r][0], ref[r][1], f"gqa_decode row {r} N={w.kv_len[r]}")
+    # the appended token is the last key of each row
+    k_slot = plan.write_slots()
+    page, off = k_slot[rows[0]] // 16, k_slot[rows[0]] % 16
+    assert torch.equal(w.cache[page, 0, off], w.k_new[rows[0]])
+
+
+def test_full_long_decode(pkv, gpu):
+    say("case long_decode full size (8 rows, N in [32768, 131072], split-KV)")
+    w = synth.make_workload("long_decode", device=gpu)
+    out, lse, plan, _ = gpu_run(pkv, w)
+    assert len(plan.merges()) > 0
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    rows = _sample_rows(w.batch, 3, 2)
+    ref = oracle_rows(w, rows)
+    for r in rows:
+        compare(out[r:r + 1], lse[r:r + 1], ref[r][0], ref[r][1], f"long_decode row {r} N={w.kv_len[r]}")
+
+
+def test_full_ragged_prefill(pkv, gpu):
+    say("case ragged_prefill full size (16 rows, q 128..2048, prefix 0..4096)")
+    w = synth.make_workload("ragged_prefill", device=gpu)
+    out, lse, plan, _ = gpu_run(pkv, w)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    rows = _sample_rows(w.batch, 4, 3)
+    rng = np.random.default_rng(4)
+    toks = {r: np.unique(np.concatenate([[0, int(w.q_len[r]) - 1],
+                                         rng.integers(0, int(w.q_len[r]), size=40)])) for r in rows}
+    ref = oracle_rows(w, rows, tokens=toks)
+    for r in rows:
+        sel = int(w.qo_indptr[r]) + toks[r]
+        compare(out[sel], lse[sel], ref[r][0], ref[r][1], f"ragged_prefill row {r} L={w.q_len[r]} N={w.kv_len[r]}")
+
+
+def test_full_mixed_window(pkv, gpu):
+    say("case mixed_window full size (256 decode rows + 4 prompt rows, window 4096)")
+    w = synth.make_workload("mixed_window", device=gpu)
+    out, lse, plan, _ = gpu_run(pkv, w)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    dec, pre, perm = oracle.mixed_permutation(w.qo_indptr, max_prefill_rows=4)
+    assert np.array_equal(plan.permutation(), perm)
+    rows = _sample_rows(len(dec), 8, 5)
+    rows = [int(dec[i]) for i in rows] + [int(dec[np.argmax(w.kv_len[dec])])]
+    rng = np.random.default_rng(6)
+    toks = {r: np.array([0]) for r in rows}
+    for r in pre[:2]:
+        r = int(r)
+        rows.append(r)
+        toks[r] = np.unique(np.concatenate([[0, 1023], rng.integers(0, 1024, size=24)]))
+    ref = oracle_rows(w, rows, tokens=toks)
+    for r in rows:
+        sel = int(w.qo_indptr[r]) + toks[r]
+        compare(out[sel], lse[sel], ref[r][0], ref[r][1], f"mixed row {r} L={w.q_len[r]} N={w.kv_len[r]}")
