@@ -35,6 +35,14 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, published
 
 METRIC = "decode KV-read GB/s (% HBM peak); prefill TFLOP/s (% bf16 MFMA peak)"
 
+# rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch) against a plain copy kernel
+# of 1 GiB on this GPU: FETCH_SIZE reads 524288 KiB for 1048576 KiB fetched,
+# WRITE_SIZE reads 1048576 KiB for 1048576 KiB written.
+FETCH_SCALE = 2.0
+WRITE_SCALE = 1.0
+CSRC = os.path.join(ROOT, "paged_kv_attention_plan_amd", "csrc")
+KERNEL_SOURCE = {"decode_kernel": "decode.hip", "prefill_kernel": "prefill.hip"}
+
 DESCR = {
     "tiny_decode": "tiny decode: 4 requests, Hq 4 / Hk 2, D 64, page 16, kv_len U[1,100]",
     "gqa_decode": "batched GQA decode + append: 128 requests, Hq 32 / Hk 8, D 128, page 16, "
@@ -46,6 +54,46 @@ DESCR = {
     "mixed_window": "mixed step, window 4096: 256 decode rows (kv_len U[256,8192]) + 4 prompt rows "
                     "(1024 on 2048 prefix), Hq 16 / Hk 16, D 64, page 32",
 }
+
+
+def _source_sha(kernel):
+    import hashlib
+    with open(os.path.join(CSRC, KERNEL_SOURCE[kernel]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_of(kernel, workload):
+    """HBM bytes per launch from the committed counter record, or None when no
+    record exists or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    return rec["bytes_per_launch"] if rec.get("source_sha256") == _source_sha(kernel) else None
+
+
+def record_traffic(fetch_csv, write_csv, kernel, workload, command):
+    """Write profiles/traffic_<kernel>_<workload>.json from the two rocprofv3
+    --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch)."""
+    import csv
+
+    def mean_of(path, counter):
+        vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+                if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        return sum(vals) / len(vals), len(vals)
+
+    fk, fn = mean_of(fetch_csv, "FETCH_SIZE")
+    wk, wn = mean_of(write_csv, "WRITE_SIZE")
+    rec = {"kernel": kernel, "workload": workload, "source_sha256": _source_sha(kernel),
+           "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk, "dispatches": [fn, wn],
+           "fetch_scale": FETCH_SCALE, "write_scale": WRITE_SCALE,
+           "bytes_per_launch": int(round((fk * FETCH_SCALE + wk * WRITE_SCALE) * 1024)),
+           "command": command}
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(path, rec["bytes_per_launch"])
 
 
 def visible_counts(w):
@@ -81,7 +129,7 @@ def work_of(w):
 class Runner:
     """Holds the device buffers and the plan for one workload."""
 
-    def __init__(self, name, dev):
+    def __init__(self, name, dev, tiles_per_cu=0, min_chunk_pages=0):
         import torch
         import synth
         from paged_kv_attention_plan_amd import pkv
@@ -99,7 +147,9 @@ class Runner:
                                       num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
                                       page_size=w.page_size, max_pages=w.max_pages,
                                       causal=w.causal, window_left=w.window_left,
-                                      max_prefill_rows=w.max_prefill_rows)
+                                      max_prefill_rows=w.max_prefill_rows,
+                                      decode_tiles_per_cu=tiles_per_cu,
+                                      decode_min_chunk_pages=min_chunk_pages)
         self.plan = pkv.plan_create(self.params, self.qo, w.kv_indptr, w.kv_indices,
                                     w.last_page_len)
         self.ws = torch.empty(self.plan.ws_bytes, dtype=torch.uint8, device=dev)
@@ -145,9 +195,10 @@ class Runner:
         return {k: (ms / n if n else None, n) for k, (ms, n) in res.items()}
 
 
-def cpu_baseline(runner, budget_s=12.0):
+def cpu_baseline(runner, unit, budget_s=12.0):
     """The oracle, timed on the host on the first rows of the same inputs until
-    about budget_s seconds of work; returns the same unit as the metric."""
+    about budget_s seconds of work; reported in the metric's unit (GB/s of KV
+    read for decode workloads, TFLOP/s for prefill)."""
     import torch
     import oracle
     w = runner.w
@@ -157,6 +208,7 @@ def cpu_baseline(runner, budget_s=12.0):
         cores = max(blas) if blas else 1
     except Exception:
         cores = 1
+    vis = visible_counts(w)
     done, kv_bytes, flops, elapsed = 0, 0, 0, 0.0
     for r in range(w.batch):
         pages = w.kv_indices[w.kv_indptr[r]:w.kv_indptr[r + 1]]
@@ -170,13 +222,13 @@ def cpu_baseline(runner, budget_s=12.0):
                               qo_indptr=np.array([0, q1 - q0]), causal=w.causal,
                               window_left=w.window_left)
         elapsed += time.perf_counter() - t0
-        n = int(w.kv_len[r])
-        kv_bytes += n * w.num_kv_heads * w.head_dim * 4
+        kv_bytes += int(vis[q0:q1].max(initial=0)) * w.num_kv_heads * w.head_dim * 4
+        flops += int(vis[q0:q1].sum()) * w.num_qo_heads * 4 * w.head_dim
         done += 1
         if elapsed >= budget_s:
             break
-    return {"value": round(kv_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle",
+    value = kv_bytes / elapsed / 1e9 if unit == "GB/s" else flops / elapsed / 1e12
+    return {"value": round(value, 6), "unit": unit, "cores": int(cores), "kind": "oracle",
             "sample": f"first {done} of {w.batch} requests of the same seeded input, every query "
                       f"head (float64 numpy), {elapsed:.1f} s"}
 
@@ -213,7 +265,17 @@ def main():
     ap.add_argument("--config", default="gqa_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--tiles-per-cu", type=int, default=0,
+                    help="split-KV planner knob (0 = library default)")
+    ap.add_argument("--min-chunk-pages", type=int, default=0,
+                    help="split-KV planner knob (0 = library default)")
+    ap.add_argument("--record-traffic", nargs=5,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "KERNEL", "WORKLOAD", "COMMAND"),
+                    help="write the traffic record of a kernel from two rocprofv3 --pmc csv files")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU code "
               "(see DESIGN.md for how it would shard).", file=sys.stderr)
@@ -223,17 +285,32 @@ def main():
     from paged_kv_attention_plan_amd import pkv  # noqa: F401  (fails loudly if not built)
     dev = torch.device("cuda:0")
 
-    r = Runner(args.config, dev)
+    r = Runner(args.config, dev, args.tiles_per_cu, args.min_chunk_pages)
     ms, wall_ms = r.time_steps(args.steps, args.warmup)
     kt = r.kernel_times(args.steps)
     w = r.work
-    value = w["kv_bytes"] / (ms * 1e-3) / 1e9
-    dec_ms = kt["decode"][0]
-    achieved = w["decode_bytes"] / (dec_ms * 1e-3) / 1e9
+    if w["kv_bytes"]:  # decode rows present: KV bytes per second, decode kernel on HBM
+        value, unit = w["kv_bytes"] / (ms * 1e-3) / 1e9, "GB/s"
+        dec_ms = kt["decode"][0]
+        achieved = w["decode_bytes"] / (dec_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_of("decode_kernel", args.config),
+                "kernel": "decode_kernel", "kernel_us": round(dec_ms * 1e3, 2),
+                "bytes_per_launch": w["decode_bytes"]}
+    else:  # prefill only: FLOP per second, prefill kernel on bf16 MFMA
+        value, unit = w["prefill_flops"] / (ms * 1e-3) / 1e12, "TFLOP/s"
+        pre_ms = kt["prefill"][0]
+        achieved = w["prefill_flops"] / (pre_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
+                "traffic": traffic_of("prefill_kernel", args.config), "kernel": "prefill_kernel",
+                "kernel_us": round(pre_ms * 1e3, 2),
+                "flops_per_launch": w["prefill_flops"]}
     line = {
         "metric": METRIC,
         "value": round(value, 2),
-        "unit": "GB/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -244,15 +321,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": DESCR[args.config], "kv_bytes_per_step": w["kv_bytes"],
+                   "prefill_flops_per_step": w["prefill_flops"],
                    "step": "plan_update + upload + append_kv + run (decode + split-KV merge)"
                    if r.append else "plan_update + upload + run"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_kernel", "kernel_us": round(dec_ms * 1e3, 2),
-                     "bytes_per_launch": w["decode_bytes"]},
+        "roofline": roof,
         "kernels_us": {k: (round(v[0] * 1e3, 2) if v[0] is not None else None)
                        for k, v in kt.items()},
         "host_ms_per_step": round(wall_ms, 4),
+        "plan": r.plan.info(),
     }
     if not args.no_secondary:
         sec = []
@@ -261,7 +337,7 @@ def main():
                 sec.append(secondary(name, dev, max(5, args.steps // 5), 2))
         line["secondary"] = sec
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(r)
+        line["cpu_baseline"] = cpu_baseline(r, unit)
     print(json.dumps(line), flush=True)
 
 

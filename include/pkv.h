@@ -103,7 +103,7 @@ typedef struct pkv_plan_params {
   int32_t num_cus;              /* compute units the plan balances over; 0 = ask the current HIP
                                    device (the workspace page: plan size depends on the SM count) */
   int64_t max_pages;            /* pages in the layer slice; page ids must be below it */
-  int32_t decode_tiles_per_cu;  /* split-KV target: at most this many decode tiles per CU; 0 = 16 */
+  int32_t decode_tiles_per_cu;  /* split-KV target: at most this many decode tiles per CU; 0 = 32 */
   int32_t decode_min_chunk_pages; /* smallest split-KV chunk, in pages; 0 = 8 */
 } pkv_plan_params;
 

@@ -16,7 +16,9 @@ Policy (the same rules the header documents):
   decode rows   visible keys [lo, N-1]; pages fp = lo // ps .. lp = (N-1) // ps.
                 chunk = min_chunk_pages * 2^k, the smallest with
                 Hk * sum_r ceil(pages_r / chunk) <= tiles_per_cu * num_cus, or
-                the first reaching the longest row.  Rows sorted by visible pages
+                the first reaching the longest row.  A row of v pages is cut into
+                n = ceil(v / chunk) chunks, chunk i holding pages
+                [floor(i*v/n), floor((i+1)*v/n)).  Rows sorted by visible pages
                 descending (ties: row index); per row chunk-major, head-minor.
                 Rows with more than one chunk get Hk * n_chunks consecutive
                 partial slots, head-major.
@@ -48,7 +50,7 @@ def split_rows(kind, layout, max_prefill_rows=0):
 
 
 def decode_policy(layout, rows, *, page_size, num_kv_heads, window_left, num_cus, qo_indptr,
-                  kv_indptr, tiles_per_cu=16, min_chunk_pages=8):
+                  kv_indptr, tiles_per_cu=32, min_chunk_pages=8):
     """Expected decode tiles and merges.
 
     Returns (tiles, merges, chunk_pages, n_slots) with tiles as tuples
@@ -81,8 +83,8 @@ def decode_policy(layout, rows, *, page_size, num_kv_heads, window_left, num_cus
         nch = -(-vis // chunk)
         base = slot if nch > 1 else -1
         for i in range(nch):
-            ks = max(lo, (fp + i * chunk) * ps)
-            ke = min(n, (fp + (i + 1) * chunk) * ps)
+            ks = max(lo, (fp + i * vis // nch) * ps)
+            ke = min(n, (fp + (i + 1) * vis // nch) * ps)
             for hk in range(num_kv_heads):
                 out_slot = base + hk * nch + i if nch > 1 else -1
                 tiles.append((r, hk, ks, ke, int(kv_indptr[r]), int(qo_indptr[r]), out_slot, n))

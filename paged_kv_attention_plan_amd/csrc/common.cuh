@@ -52,6 +52,24 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal (streamed once: keeps the caches for other data).
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 constexpr float kLn2 = 0.69314718055994530942f;
+
+// Read-only data viewed through the constant address space: uniform loads from
+// it go through the scalar unit (s_load), whatever else the kernel does.
+template <typename T>
+using const_as4_ptr = const __attribute__((address_space(4))) T*;
+
+template <typename T>
+__device__ __forceinline__ const_as4_ptr<T> as_const4(const T* p) {
+  return reinterpret_cast<const_as4_ptr<T>>(reinterpret_cast<uintptr_t>(p));
+}
 
 }  // namespace pkv

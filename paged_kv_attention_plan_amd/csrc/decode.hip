@@ -6,7 +6,8 @@
 // spread over LPK = D/8 lanes, 16 bytes each, so one wave-wide load fetches
 // KPL = 64/LPK whole key rows with fully used 16-byte lane accesses.  An
 // iteration issues U such loads for K and U for V (KB = KPL*U keys) and the
-// next iteration's loads go out before the current one is computed.
+// next iteration's loads go out before the current one is computed.  K and V
+// are streamed once, so they are loaded non-temporal.
 //
 // Scores: each lane forms the partial dot product of its 8 dimensions with the
 // group's G query heads (bf16 dot2), then a DPP allreduce over its LPK lanes.
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 
   const int lk = lane / LPK;   // key row within a load
   const int ld = lane % LPK;   // 8-element segment of head_dim
-  const int lane_off = hk * D + ld * 8;
+  const uint32_t lane_off = hk * D + ld * 8;
 
   // Query heads hk*G .. hk*G+G-1, this lane's 8 dimensions, as packed bf16 pairs.
   uint32_t qw[G][4];
@@ -66,6 +67,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       qw[h][0] = v.x; qw[h][1] = v.y; qw[h][2] = v.z; qw[h][3] = v.w;
     }
   }
+  // Let q land before the key loop starts, so every path into the loop has the
+  // same loads in flight (otherwise the loop head waits for everything): an
+  // empty asm that reads the q registers makes the compiler wait for them here.
+#pragma unroll
+  for (int h = 0; h < G; ++h) asm volatile("" ::"v"(qw[h][0]), "v"(qw[h][1]), "v"(qw[h][2]), "v"(qw[h][3]));
+  __builtin_amdgcn_sched_barrier(0);
 
   float m[G], l[G], o[G][8];
 #pragma unroll
@@ -76,50 +83,53 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
   }
 
+  // Key blocks of KB keys: block b starts at kb0 + b*KB; the last one holds key ke-1.
   const int kb0 = ks & ~(KB - 1);
-  // Physical page ids of the chunk, 64 at a time: lane i holds logical page
-  // win + i of the row.
-  const int last_lp = (ke - 1) >> ps_log2;
-  int win = kb0 >> ps_log2;
-  int pid_vec = 0;
-  {
-    const int i = win + lane;
-    pid_vec = i <= last_lp ? a.indices[page_base + i] : 0;
-  }
+  const int nb = (((ke - 1) & ~(KB - 1)) - kb0) / KB + 1;
 
-  uint4 kr[U], vr[U];
-  auto issue = [&](int kb, uint4 (&kk)[U], uint4 (&vv)[U]) {
+  // Physical page of block b (one page per block): a uniform load through the
+  // scalar unit, fetched one block ahead of the loads that use it.
+  const_as4_ptr<int32_t> cidx = as_const4(a.indices);
+  uint32_t lane_byte[U];  // byte offset of this lane's 16 bytes within a block
+#pragma unroll
+  for (int u = 0; u < U; ++u) lane_byte[u] = ((u * KPL + lk) * (uint32_t)row_elems + lane_off) * 2u;
+  auto page_of = [&](int b) -> int {
+    b = b < nb ? b : nb - 1;
+    return cidx[page_base + ((kb0 + b * KB) >> ps_log2)];
+  };
+
+  // Issue the K and V loads of block b (clamped to the last block, so the
+  // number of loads in flight is the same on every path).
+  auto issue = [&](int b, int phys, uint4 (&kk)[U], uint4 (&vv)[U]) {
+    b = b < nb ? b : nb - 1;
+    const int kb = kb0 + b * KB;
     if constexpr (ONE_PAGE_PER_ITER) {
-      const int lp = kb >> ps_log2;
-      if (lp - win >= 64) {  // uniform: next window of page ids
-        win += 64;
-        const int i = win + lane;
-        pid_vec = i <= last_lp ? a.indices[page_base + i] : 0;
-      }
-      const int phys = __builtin_amdgcn_readlane(pid_vec, lp - win);
-      const uint16_t* pbase = a.cache + (int64_t)phys * page_elems;
-      const int slot0 = kb & (ps - 1);
+      // Uniform base (page and slot, scalar registers) + a loop-invariant 32-bit
+      // byte offset per lane: no address arithmetic per block in vector registers.
+      const char* kbase = reinterpret_cast<const char*>(a.cache) +
+                          ((int64_t)phys * page_elems + (int64_t)(kb & (ps - 1)) * row_elems) * 2;
+      const char* vbase = kbase + (int64_t)v_off * 2;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int off = (slot0 + u * KPL + lk) * row_elems + lane_off;
-        kk[u] = *reinterpret_cast<const uint4*>(pbase + off);
-        vv[u] = *reinterpret_cast<const uint4*>(pbase + off + v_off);
+        kk[u] = load_nt16(kbase + lane_byte[u]);
+        vv[u] = load_nt16(vbase + lane_byte[u]);
       }
     } else {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         int j = kb + u * KPL + lk;
         j = j < ke ? j : ke - 1;  // keys past the chunk are masked; keep the address valid
-        const int phys = a.indices[page_base + (j >> ps_log2)];
-        const uint16_t* p = a.cache + (int64_t)phys * page_elems +
-                            (j & (ps - 1)) * row_elems + lane_off;
-        kk[u] = *reinterpret_cast<const uint4*>(p);
-        vv[u] = *reinterpret_cast<const uint4*>(p + v_off);
+        const int pg = a.indices[page_base + (j >> ps_log2)];
+        const uint16_t* p = a.cache + (int64_t)pg * page_elems + (j & (ps - 1)) * row_elems +
+                            lane_off;
+        kk[u] = load_nt16(p);
+        vv[u] = load_nt16(p + v_off);
       }
     }
   };
 
-  auto compute = [&](const uint4 (&kk)[U], const uint4 (&vv)[U], int kb) {
+  auto compute = [&](const uint4 (&kk)[U], const uint4 (&vv)[U], int b) {
+    const int kb = kb0 + b * KB;
     float s[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -132,26 +142,16 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         s[u][h] = group_sum<LPK>(acc) * a.scale_log2;
       }
     }
-    float vf[U][8];
+    const bool edge = kb < ks || kb + KB > ke;  // uniform: a chunk edge
+    bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      vf[u][0] = bf16_lo(vv[u].x); vf[u][1] = bf16_hi(vv[u].x);
-      vf[u][2] = bf16_lo(vv[u].y); vf[u][3] = bf16_hi(vv[u].y);
-      vf[u][4] = bf16_lo(vv[u].z); vf[u][5] = bf16_hi(vv[u].z);
-      vf[u][6] = bf16_lo(vv[u].w); vf[u][7] = bf16_hi(vv[u].w);
+      const int j = kb + u * KPL + lk;
+      ok[u] = !edge || (j >= ks && j < ke);
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[u][h] = ok[u] ? s[u][h] : -INFINITY;
     }
-    if (kb < ks || kb + KB > ke) {  // uniform: chunk edges
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = kb + u * KPL + lk;
-        if (j < ks || j >= ke) {
-#pragma unroll
-          for (int h = 0; h < G; ++h) s[u][h] = -INFINITY;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) vf[u][e] = 0.f;  // stale slots may hold NaN
-        }
-      }
-    }
+    // New running max per head; rescale what was accumulated so far.
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float mx = s[0][h];
@@ -160,31 +160,50 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       const float mn = fmaxf(m[h], mx);
       const float alpha = fast_exp2(m[h] - mn);
       m[h] = mn;
-      float lsum = l[h] * alpha;
+      l[h] *= alpha;
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+    }
+    // One key row at a time: widen its V once, use it for every head.
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float p = fast_exp2(s[u][h] - mn);
-        lsum += p;
+    for (int u = 0; u < U; ++u) {
+      float vf[8];
+      vf[0] = bf16_lo(vv[u].x); vf[1] = bf16_hi(vv[u].x);
+      vf[2] = bf16_lo(vv[u].y); vf[3] = bf16_hi(vv[u].y);
+      vf[4] = bf16_lo(vv[u].z); vf[5] = bf16_hi(vv[u].z);
+      vf[6] = bf16_lo(vv[u].w); vf[7] = bf16_hi(vv[u].w);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vf[u][e], o[h][e]);
+      for (int e = 0; e < 8; ++e) vf[e] = ok[u] ? vf[e] : 0.f;  // stale slots may hold NaN
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = fast_exp2(s[u][h] - m[h]);
+        l[h] += p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vf[e], o[h][e]);
       }
-      l[h] = lsum;
     }
   };
 
-  issue(kb0, kr, vr);
-  for (int kb = kb0; kb < ke; kb += KB) {
-    uint4 kn[U], vn[U];
-    const bool more = kb + KB < ke;
-    if (more) issue(kb + KB, kn, vn);
-    compute(kr, vr, kb);
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) { kr[u] = kn[u]; vr[u] = vn[u]; }
-    }
+  // Two register buffers: one block's loads are in flight while the other is
+  // computed.  Each trip computes two blocks and has a single exit at the top (a
+  // mid-loop exit would give the loop head a path with other loads in flight,
+  // and the compiler would then wait for all of them there).  The scheduling
+  // barriers keep compute from being hoisted above the loads.
+  uint4 ka[U], va[U], kbuf[U], vbuf[U];
+  issue(0, ONE_PAGE_PER_ITER ? page_of(0) : 0, ka, va);
+  int pid = ONE_PAGE_PER_ITER ? page_of(1) : 0;
+  int b = 0;
+  for (; b + 1 < nb; b += 2) {
+    issue(b + 1, pid, kbuf, vbuf);
+    pid = ONE_PAGE_PER_ITER ? page_of(b + 2) : 0;
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ka, va, b);
+    issue(b + 2, pid, ka, va);  // past the end: a clamped, cached reload, never computed
+    pid = ONE_PAGE_PER_ITER ? page_of(b + 3) : 0;
+    __builtin_amdgcn_sched_barrier(0);
+    compute(kbuf, vbuf, b + 1);
   }
+  if (b < nb) compute(ka, va, b);  // odd block count: the last block is in A
 
   // Combine the KPL lane groups (lanes that differ in bits >= log2(LPK)).
 #pragma unroll

@@ -17,30 +17,53 @@ namespace {
 
 constexpr int kWaves = 4;
 
+// One workgroup per (merge entry, query head).  The log-sum-exp of all chunks
+// is found first (every lane reads a strided subset of the chunk LSEs); then
+// each wave accumulates a quarter of the chunks with all of its loads
+// independent, and the four partial sums are added through LDS.
 template <int D>
 __global__ __launch_bounds__(64 * kWaves) void merge_kernel(MergeArgs a) {
-  constexpr int E = D / 64;  // elements per lane
+  constexpr int E = D / 64;  // output elements per lane
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = a.group;
-  const int item = blockIdx.x * kWaves + wave;  // (merge entry, head in group)
-  if (item >= a.n_merges * G) return;
-  const int mi = item / G, h = item - mi * G;
+  const int mi = blockIdx.x / G, h = blockIdx.x - mi * G;
   const pkv_merge_entry e = a.merges[mi];
+  const int n = e.n_chunks;
   const float* pl = a.part_lse + (int64_t)e.slot_base * G + h;
+  __shared__ float red[kWaves][D + 1];
+  __shared__ float s_max[kWaves];
+
   float M = -INFINITY;
-  for (int c = 0; c < e.n_chunks; ++c) M = fmaxf(M, pl[(int64_t)c * G]);
+  for (int c = threadIdx.x; c < n; c += 64 * kWaves) M = fmaxf(M, pl[(int64_t)c * G]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) s_max[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+
   float wsum = 0.f, acc[E];
 #pragma unroll
   for (int k = 0; k < E; ++k) acc[k] = 0.f;
-  for (int c = 0; c < e.n_chunks; ++c) {
+  const float* po = a.part_o + ((int64_t)e.slot_base * G + h) * D + lane * E;
+  const int64_t cstride = (int64_t)G * D;
+#pragma unroll 4
+  for (int c = wave; c < n; c += kWaves) {
     const float wc = __expf(pl[(int64_t)c * G] - M);
     wsum += wc;
-    const float* po = a.part_o + ((int64_t)(e.slot_base + c) * G + h) * D + lane * E;
 #pragma unroll
-    for (int k = 0; k < E; ++k) acc[k] = fmaf(wc, po[k], acc[k]);
+    for (int k = 0; k < E; ++k) acc[k] = fmaf(wc, po[c * cstride + k], acc[k]);
   }
-  const float inv = 1.f / wsum;
+#pragma unroll
+  for (int k = 0; k < E; ++k) red[wave][lane * E + k] = acc[k];
+  if (lane == 0) red[wave][D] = wsum;
+  __syncthreads();
+  if (wave != 0) return;
+  float tot = red[0][D] + red[1][D] + red[2][D] + red[3][D];
+#pragma unroll
+  for (int k = 0; k < E; ++k)
+    acc[k] = red[0][lane * E + k] + red[1][lane * E + k] + red[2][lane * E + k] + red[3][lane * E + k];
+  const float inv = 1.f / tot;
   const int qh = e.kv_head * G + h;
   uint16_t* dst = a.out + ((int64_t)e.q_index * a.num_qo_heads + qh) * D + lane * E;
   if constexpr (E == 2) {
@@ -49,7 +72,7 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(MergeArgs a) {
     dst[0] = (uint16_t)bf16_rne(acc[0] * inv);
   }
   if (a.lse != nullptr && lane == 0)
-    a.lse[(int64_t)e.q_index * a.num_qo_heads + qh] = M + logf(wsum);
+    a.lse[(int64_t)e.q_index * a.num_qo_heads + qh] = M + logf(tot);
 }
 
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
@@ -74,8 +97,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   if (a.n_merges <= 0) return hipSuccess;
-  const int items = a.n_merges * a.group;
-  const dim3 grid((items + kWaves - 1) / kWaves), block(64 * kWaves);
+  const dim3 grid(a.n_merges * a.group), block(64 * kWaves);
   if (a.head_dim == 128) hipLaunchKernelGGL(merge_kernel<128>, grid, block, 0, stream, a);
   else if (a.head_dim == 64) hipLaunchKernelGGL(merge_kernel<64>, grid, block, 0, stream, a);
   else return hipErrorInvalidValue;

@@ -11,8 +11,10 @@
 //          lo/ps to (N-1)/ps.  The split-KV chunk C (pages) is the smallest
 //          min_chunk_pages * 2^k for which Hk * sum_r ceil(pages_r / C) fits
 //          tiles_per_cu * num_cus, or the first that reaches the longest row.
-//          Rows are taken longest first (ties: lower row index); a row's tiles
-//          are chunk-major, KV-head-minor.  A row cut into n > 1 chunks owns
+//          A row of v visible pages is cut into n = ceil(v / C) chunks of
+//          nearly equal size: chunk i holds pages [i*v/n, (i+1)*v/n) (floor),
+//          so no tile is a short remainder.  Rows are taken longest first
+//          (ties: lower row index); a row's tiles are chunk-major, KV-head-minor.  A row cut into n > 1 chunks owns
 //          Hk * n consecutive partial slots (head-major) and one merge per head.
 //  prefill Query tokens are taken in blocks of 128/group so a block fills the
 //          128 rows of a kernel tile; a block's keys are [lo of its first token,
@@ -230,7 +232,7 @@ pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
   }
 
   // ---- decode tiles and split-KV chunks ----
-  const int32_t tiles_per_cu = P.decode_tiles_per_cu > 0 ? P.decode_tiles_per_cu : 16;
+  const int32_t tiles_per_cu = P.decode_tiles_per_cu > 0 ? P.decode_tiles_per_cu : 32;
   const int32_t min_chunk = P.decode_min_chunk_pages > 0 ? P.decode_min_chunk_pages : 8;
   struct DecRow { int32_t r; int64_t lo, fp, lp, vis; };
   std::vector<DecRow> drows;
@@ -262,8 +264,9 @@ pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
     const int64_t nch = (d.vis + chunk - 1) / chunk;
     const int64_t base = slot;
     for (int64_t i = 0; i < nch; ++i) {
-      const int64_t ks = std::max(d.lo, (d.fp + i * chunk) * ps);
-      const int64_t ke = std::min(n, (d.fp + (i + 1) * chunk) * ps);
+      const int64_t p0 = d.fp + i * d.vis / nch, p1 = d.fp + (i + 1) * d.vis / nch;
+      const int64_t ks = std::max(d.lo, p0 * ps);
+      const int64_t ke = std::min(n, p1 * ps);
       for (int32_t hk = 0; hk < Hk; ++hk) {
         pkv_decode_tile t;
         t.row = d.r;

@@ -6,13 +6,18 @@
 // A workgroup (4 waves) owns one tile: a row, a KV head and a block of BT =
 // 128/group query tokens, i.e. 128 (query head, token) pairs that all read the
 // same K/V.  Wave w takes pairs 32w..32w+31.  Keys are consumed 64 at a time:
-// the workgroup gathers the 64 key rows from their pages into LDS -- K as rows
-// [key][d], V transposed [d][key] -- and every wave then computes
+// the workgroup gathers the 64 key rows of K and V from their pages into LDS,
+// both as rows [key][d], and every wave then computes
 //   S^T (64 keys x 32 queries) = K . Q^T       (A = K from LDS, B = Q in registers)
 //   P = exp2(S*scale*log2e - m)                (online softmax, fp32, per query column)
-//   O^T (D x 32 queries)     += V^T . P^T      (A = V^T from LDS, B = P as bf16)
+//   O^T (D x 32 queries)     += V^T . P^T      (A = V^T, read transposed from LDS
+//                                                by ds_read_b64_tr_b16; B = P as bf16)
 // With S^T a lane holds one query column, so the row max needs a single
 // cross-half exchange and the per-query rescale is a per-lane scalar.
+//
+// The running max is only moved when some query's new maximum exceeds it by
+// more than 2^8 (in exp2 units): P stays <= 256, harmless in fp32 and bf16,
+// and the O rescale (64 multiplies per lane) is skipped on most key tiles.
 #include "common.cuh"
 #include "kernels.h"
 
@@ -23,8 +28,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kRescaleSlack = 8.f;  // log2 units: P may reach 2^8 before O is rescaled
 
 __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -36,25 +42,34 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
 }
 
-// Two bf16 of different keys at the same dimension, packed (key a low, key b high).
-__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane L receives element L%4 of
+// the 4-element (8-byte) rows addressed by lanes L/4, L/4+4, L/4+8, L/4+12, in
+// that order.  With lane a of the group pointing at row (key0 + a/4) and column
+// (d0 + 4*(a%4)) of a [key][d] tile, lane 4m+j receives column d0 + 4m + j at
+// keys key0 .. key0+3: a column of V, four keys long.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
+  // p points into __shared__ memory; the C-style cast converts it to an LDS address.
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(u32x2_t, v);
 }
 
-template <int D>
+// WAVE_PAGE: page_size >= 16, so the 16 keys a wave stages per tile lie in one
+// page -- its id is a scalar load and the loads use a scalar base.
+template <int D, bool WAVE_PAGE>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int BN = 64;              // keys per iteration
   constexpr int KSTEPS = D / 16;      // MFMA steps over head_dim for S
   constexpr int DBLK = D / 32;        // 32-row output blocks over head_dim
   constexpr int SEGS = D / 8;         // 16-byte segments of a key row
   constexpr int KPT = BN * SEGS / 256;  // key rows each thread stages per iteration
-  constexpr int KS = D + 8;           // LDS row stride of K (elements)
-  constexpr int VS = BN + 4;          // LDS row stride of V^T (elements)
+  constexpr int KS = D + 8;           // LDS row stride of K (elements): 16-byte row reads
+  constexpr int VS = D + 16;          // LDS row stride of V (elements): the four rows a
+                                      // transposed read touches start 8 banks apart
   __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[BN * VS];
 
   const pkv_prefill_tile* tp = a.tiles + blockIdx.x;
   const int hk = tp->kv_head;
@@ -77,6 +92,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const int v_off = ps * row_elems;
   const bool causal = a.causal != 0;
   const int wl = a.window_left;
+  const float c = a.scale_log2;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -106,59 +122,89 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   f32x16_t oacc[DBLK];
 #pragma unroll
   for (int b = 0; b < DBLK; ++b) oacc[b] = f32x16_t{};
-  float m_run = -1e30f, l_run = 0.f;
+  float m_run = -1e30f, l_run = 0.f;  // m_run in exp2 units (scaled)
 
   // Block-wide query position bounds, for deciding which key tiles need masks.
   const int p_first = kv_len - q_len + q_start;
   const int p_last = p_first + q_count - 1;
 
-  // Staging map: thread -> (segment, key group of KPT keys).
+  // Staging map: thread -> (segment, key group of KPT keys).  The 16 keys of a
+  // wave are [16*wave, 16*wave + 16) of the tile.
   const int seg = threadIdx.x % SEGS;
   const int kg = threadIdx.x / SEGS;
-  u32x4_t gk[KPT], gv[KPT];
-  auto gload = [&](int kbase) {
+  const int kstart = kv_lo & ~(BN - 1);
+  const int kend = kv_hi + 1;
+  const int ntiles = (kend - kstart + BN - 1) / BN;
+  const_as4_ptr<int32_t> cidx = as_const4(a.indices);
+  const uint32_t row_bytes = (uint32_t)row_elems * 2u;
+  const int64_t head_bytes = (int64_t)hk * D * 2;
+
+  // Key i of this thread in tile t (clamped to the last tile and the last key,
+  // so addresses stay inside the row; keys past the row are masked later).
+  auto key_of = [&](int t, int i) {
+    t = t < ntiles ? t : ntiles - 1;
+    const int key = kstart + t * BN + kg * KPT + i;
+    return key < kv_len ? key : kv_len - 1;
+  };
+  auto load_pids = [&](int t, int (&pid)[KPT]) {
+    if constexpr (WAVE_PAGE) {
+      const int tt = t < ntiles ? t : ntiles - 1;
+      int k0 = kstart + tt * BN + 16 * wave;
+      k0 = k0 < kv_len ? k0 : kv_len - 1;
+      pid[0] = cidx[page_base + (k0 >> ps_log2)];  // uniform: scalar load
+    } else {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      int key = kbase + kg * KPT + i;
-      key = key < kv_len ? key : kv_len - 1;  // past the row: masked later, address kept valid
-      const int phys = a.indices[page_base + (key >> ps_log2)];
-      const uint16_t* p = a.cache + (int64_t)phys * page_elems + (key & (ps - 1)) * row_elems +
-                          hk * D + seg * 8;
-      gk[i] = *reinterpret_cast<const u32x4_t*>(p);
-      gv[i] = *reinterpret_cast<const u32x4_t*>(p + v_off);
+      for (int i = 0; i < KPT; ++i) pid[i] = cidx[page_base + (key_of(t, i) >> ps_log2)];
+    }
+  };
+  u32x4_t gk[KPT], gv[KPT];
+  auto gload = [&](int t, const int (&pid)[KPT]) {
+    if constexpr (WAVE_PAGE) {
+      const char* kb = reinterpret_cast<const char*>(a.cache) + (int64_t)pid[0] * page_elems * 2 +
+                       head_bytes;
+      const char* vb = kb + (int64_t)v_off * 2;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const uint32_t off = (uint32_t)(key_of(t, i) & (ps - 1)) * row_bytes + seg * 16u;
+        gk[i] = *reinterpret_cast<const u32x4_t*>(kb + off);
+        gv[i] = *reinterpret_cast<const u32x4_t*>(vb + off);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int key = key_of(t, i);
+        const uint16_t* p = a.cache + (int64_t)pid[i] * page_elems +
+                            (key & (ps - 1)) * row_elems + hk * D + seg * 8;
+        gk[i] = *reinterpret_cast<const u32x4_t*>(p);
+        gv[i] = *reinterpret_cast<const u32x4_t*>(p + v_off);
+      }
     }
   };
   auto swrite = [&]() {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i)
+    for (int i = 0; i < KPT; ++i) {
       *reinterpret_cast<u32x4_t*>(&sK[(kg * KPT + i) * KS + seg * 8]) = gk[i];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {  // dword w of a key row holds d = seg*8 + 2w, 2w+1
-      if constexpr (KPT == 4) {
-        const uint32_t x0 = gv[0][w], x1 = gv[1][w], x2 = gv[2][w], x3 = gv[3][w];
-        const u32x2_t lo = {lo_halves(x0, x1), lo_halves(x2, x3)};
-        const u32x2_t hi = {hi_halves(x0, x1), hi_halves(x2, x3)};
-        *reinterpret_cast<u32x2_t*>(&sV[(seg * 8 + 2 * w) * VS + kg * 4]) = lo;
-        *reinterpret_cast<u32x2_t*>(&sV[(seg * 8 + 2 * w + 1) * VS + kg * 4]) = hi;
-      } else {
-        const uint32_t x0 = gv[0][w], x1 = gv[1][w];
-        *reinterpret_cast<uint32_t*>(&sV[(seg * 8 + 2 * w) * VS + kg * 2]) = lo_halves(x0, x1);
-        *reinterpret_cast<uint32_t*>(&sV[(seg * 8 + 2 * w + 1) * VS + kg * 2]) = hi_halves(x0, x1);
-      }
+      *reinterpret_cast<u32x4_t*>(&sV[(kg * KPT + i) * VS + seg * 8]) = gv[i];
     }
   };
 
-  const int kstart = kv_lo & ~(BN - 1);
-  const int kend = kv_hi + 1;
-  const int ntiles = (kend - kstart + BN - 1) / BN;
-
-  gload(kstart);
+  // Pipeline: the data of tile it+1 is loaded while tile it is computed, and
+  // the page ids of tile it+2 one tile earlier still, so no page-id load sits
+  // in front of a data load.
+  int pid_next[KPT];
+  {
+    int pid0[KPT];
+    load_pids(0, pid0);
+    gload(0, pid0);
+  }
+  load_pids(1, pid_next);
   for (int it = 0; it < ntiles; ++it) {
     const int kbase = kstart + it * BN;
     __syncthreads();  // every wave is done reading the previous tile
     swrite();
+    gload(it + 1, pid_next);  // clamped past the end: the loads in flight are the same every trip
+    load_pids(it + 2, pid_next);
     __syncthreads();
-    if (it + 1 < ntiles) gload(kbase + BN);
 
     // ---- S^T = K . Q^T ----
     f32x16_t sacc[2];
@@ -177,28 +223,33 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     // sacc[kb2][r] is key kbase + 32 kb2 + 8 (r/4) + 4 half + r%4 for query jcol.
     const bool need_mask = (kbase + BN - 1 > (causal ? p_first : kv_len - 1)) ||
                            (kbase + BN > kv_len) || (wl >= 0 && kbase < p_last - wl);
-    float sv[2][16];
-    float mt = -INFINITY;
+    if (need_mask) {  // uniform: the tile crosses the diagonal, the window edge or the row end
+      const int k0 = kbase + 4 * half;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sacc[kb2][r] * a.scale_log2;
-        if (need_mask) {
-          const int key = kbase + 32 * kb2 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key > hi_j || key < lo_j) x = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * kb2 + 8 * (r >> 2) + (r & 3);
+          sacc[kb2][r] = (key > hi_j || key < lo_j) ? -INFINITY : sacc[kb2][r];
         }
-        sv[kb2][r] = x;
-        mt = fmaxf(mt, x);
-      }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(m_run, mt);
-    const float alpha = fast_exp2(m_run - mn);
-    m_run = mn;
-    l_run *= alpha;
+    // Max over the raw scores (the scale is positive, so order is kept), then scaled.
+    float mr = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
-    for (int b = 0; b < DBLK; ++b) oacc[b] *= alpha;
+    for (int r = 2; r < 16; r += 2) mr = fmaxf(mr, fmaxf(sacc[0][r], sacc[0][r + 1]));
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mr = fmaxf(mr, fmaxf(sacc[1][r], sacc[1][r + 1]));
+    mr = fmaxf(mr, __shfl_xor(mr, 32));
+    const float mt = mr * c;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {  // uniform
+      const float mn = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < DBLK; ++b) oacc[b] *= alpha;
+    }
+    const float neg_m = -m_run;
     u32x4_t pb[4];  // P^T operand per 16-key step s = 2 kb2 + t
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -207,7 +258,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(sv[kb2][8 * t + e] - mn);
+          p[e] = fast_exp2(fmaf(sacc[kb2][8 * t + e], c, neg_m));
           l_run += p[e];
         }
         pb[2 * kb2 + t] = u32x4_t{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]),
@@ -216,15 +267,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
 
     // ---- O^T += V^T . P^T ----
-    // Step s covers keys 16 s + {0..3, 8..11} + 4 half, matching pb[s]'s element order.
+    // Step s covers keys 16 s + {0..3, 8..11} + 4 half, matching pb[s]'s element
+    // order; the transposed reads deliver column 32 b + jcol at those keys.
+    {
+      const int grp = lane >> 4, ga = lane & 15;
+      const int key_l = 4 * (grp >> 1) + (ga >> 2);
+      const int d_l = 16 * (grp & 1) + 4 * (ga & 3);
 #pragma unroll
-    for (int b = 0; b < DBLK; ++b) {
+      for (int b = 0; b < DBLK; ++b) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint16_t* vrow = &sV[(32 * b + jcol) * VS + 16 * s + 4 * half];
-        const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow);
-        const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 8);
-        oacc[b] = mfma32(u32x4_t{v0[0], v0[1], v1[0], v1[1]}, pb[s], oacc[b]);
+        for (int s = 0; s < 4; ++s) {
+          const uint16_t* vp = &sV[(16 * s + key_l) * VS + 32 * b + d_l];
+          const u32x2_t v0 = lds_read_tr16(vp);
+          const u32x2_t v1 = lds_read_tr16(vp + 8 * VS);
+          oacc[b] = mfma32(u32x4_t{v0[0], v0[1], v1[0], v1[1]}, pb[s], oacc[b]);
+        }
       }
     }
   }
@@ -249,15 +306,23 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
+template <int D>
+hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
+  const dim3 grid(a.n_tiles), block(256);
+  if (a.page_size >= 16)
+    hipLaunchKernelGGL((prefill_kernel<D, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (a.n_tiles <= 0) return hipSuccess;
-  const dim3 grid(a.n_tiles), block(256);
-  if (a.head_dim == 128) hipLaunchKernelGGL(prefill_kernel<128>, grid, block, 0, stream, a);
-  else if (a.head_dim == 64) hipLaunchKernelGGL(prefill_kernel<64>, grid, block, 0, stream, a);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (a.head_dim == 128) return launch_d<128>(a, stream);
+  if (a.head_dim == 64) return launch_d<64>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv

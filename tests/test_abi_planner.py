@@ -60,7 +60,7 @@ def test_decode_plan_matches_policy(c):
     tiles, merges, chunk, n_slots = oracle.decode_policy(
         lay, rows, page_size=w.page_size, num_kv_heads=w.num_kv_heads, window_left=w.window_left,
         num_cus=c["num_cus"], qo_indptr=w.qo_indptr, kv_indptr=w.kv_indptr,
-        tiles_per_cu=c["tpc"] or 16, min_chunk_pages=c["mcp"] or 8)
+        tiles_per_cu=c["tpc"] or 32, min_chunk_pages=c["mcp"] or 8)
     got = [tuple(int(x) for x in t) for t in plan.decode_tiles()]
     assert got == tiles
     assert [tuple(int(x) for x in m) for m in plan.merges()] == merges
