@@ -47,6 +47,7 @@
  *   pkv_plan_upload(workspace, stream)      async H2D from library-owned pinned memory
  *   per layer: pkv_append_kv(...)           optional; stores this step's K/V
  *              pkv_run(...)                 attention for every planned query
+ *          or  pkv_run_append(...)          both in one call
  * One plan serves every layer of a step.
  *
  * Ownership: the caller owns every device buffer (q, out, lse, cache, workspace,
@@ -191,9 +192,19 @@ pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_byt
  * q, kv_cache_layer, out: device pointers (layouts above); lse may be NULL.
  * workspace must be the buffer of the last pkv_plan_upload (else PKV_E_STATE).
  * Decode rows whose keys span several chunks write fp32 partials into the
- * workspace and a merge kernel combines them (attn.workspace).  Enqueued on stream. */
+ * workspace and a merge kernel combines them by log-sum-exp (attn.workspace).
+ * One upload serves any number of runs (one per layer); runs that overlap on one
+ * workspace (two streams, no ordering) race on its partials.  Enqueued on stream. */
 pkv_status pkv_run(const pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* pkv_append_kv followed by pkv_run on the same stream (attn.dense requires_kv_write:
+ * the step's K/V are stored before attention reads them).  k_new, v_new: bf16
+ * [total_q, Hk, D], 16-byte aligned, not NULL.  Errors as pkv_run and
+ * pkv_append_kv; nothing is enqueued when an argument check fails.  Enqueued on stream. */
+pkv_status pkv_run_append(const pkv_plan* plan, const void* q, const void* k_new, const void* v_new,
+                          void* kv_cache_layer, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* Store this step's K and V of every planned query token at its write slot:
  * cache[page, 0, off] = k_new[t], cache[page, 1, off] = v_new[t]
@@ -204,7 +215,7 @@ pkv_status pkv_append_kv(const pkv_plan* plan, const void* k_new, const void* v_
                          void* stream);
 
 /* Per-launch timing, a tracing aid (the wrappers' enable_nvtx flag is the pages'
- * counterpart).  While enabled, pkv_run and pkv_append_kv record a HIP event on the
+ * counterpart).  While enabled, pkv_run, pkv_run_append and pkv_append_kv record a HIP event on the
  * stream before and after every kernel they launch with this plan.
  * pkv_timing_read waits for those events, returns for each kernel kind
  * ([0] append, [1] decode, [2] split-KV merge, [3] prefill) the summed milliseconds

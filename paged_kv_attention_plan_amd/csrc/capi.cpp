@@ -262,22 +262,30 @@ pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_byt
   return PKV_OK;
 }
 
-pkv_status pkv_run(const pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
-                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  g_err.clear();
+namespace {
+
+// Argument checks shared by pkv_run and pkv_run_append.
+pkv_status check_run(const pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
+                     float* lse, void* workspace, size_t workspace_bytes) {
   if (plan == nullptr) return fail(PKV_E_INVALID, "plan must not be NULL");
   pkv_status st = check_workspace(plan, workspace, workspace_bytes);
   if (st != PKV_OK) return st;
   if (plan->uploaded_ws != workspace)
     return fail(PKV_E_STATE, "the plan was not uploaded to this workspace (call pkv_plan_upload first)");
-  const pkv::PlanData& d = plan->d;
-  if (d.total_q == 0) return PKV_OK;
+  if (plan->d.total_q == 0) return PKV_OK;
   if (q == nullptr || kv_cache_layer == nullptr || out == nullptr)
     return fail(PKV_E_INVALID, "q, kv_cache_layer and out must not be NULL");
   if (!aligned16(q) || !aligned16(kv_cache_layer) || !aligned16(out) || !aligned16(workspace))
     return fail(PKV_E_INVALID, "q, kv_cache_layer, out and workspace must be 16-byte aligned");
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
     return fail(PKV_E_INVALID, "lse must be 4-byte aligned");
+  return PKV_OK;
+}
+
+// Launch the plan's kernels (arguments already checked).
+pkv_status run_impl(const pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
+                    float* lse, void* workspace, void* stream) {
+  const pkv::PlanData& d = plan->d;
   const pkv_plan_params& P = d.params;
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -287,7 +295,8 @@ pkv_status pkv_run(const pkv_plan* plan, const void* q, const void* kv_cache_lay
   float* part_lse = reinterpret_cast<float*>(ws + d.ws.off_part_lse);
   if (!d.decode_tiles.empty()) {
     pkv::DecodeArgs a{};
-    a.tiles = reinterpret_cast<const pkv_decode_tile*>(ws + d.ws.off_decode_tiles);
+    a.tiles = reinterpret_cast<const pkv::DecodeTileMeta*>(ws + d.ws.off_decode_tiles);
+    a.rows = reinterpret_cast<const pkv::DecodeRowMeta*>(ws + d.ws.off_decode_rows);
     a.n_tiles = (int32_t)d.decode_tiles.size();
     a.indices = indices;
     a.q = static_cast<const uint16_t*>(q);
@@ -343,6 +352,32 @@ pkv_status pkv_run(const pkv_plan* plan, const void* q, const void* kv_cache_lay
     PKV_HIP(timing_mark(plan, s, kPrefill, false));
   }
   return PKV_OK;
+}
+
+}  // namespace
+
+pkv_status pkv_run(const pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
+                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  pkv_status st = check_run(plan, q, kv_cache_layer, out, lse, workspace, workspace_bytes);
+  if (st != PKV_OK || plan->d.total_q == 0) return st;
+  return run_impl(plan, q, kv_cache_layer, out, lse, workspace, stream);
+}
+
+pkv_status pkv_run_append(const pkv_plan* plan, const void* q, const void* k_new, const void* v_new,
+                          void* kv_cache_layer, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  pkv_status st = check_run(plan, q, kv_cache_layer, out, lse, workspace, workspace_bytes);
+  if (st != PKV_OK || plan->d.total_q == 0) return st;
+  if (k_new == nullptr || v_new == nullptr)
+    return fail(PKV_E_INVALID, "k_new and v_new must not be NULL");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(PKV_E_INVALID, "k_new and v_new must be 16-byte aligned");
+  // Every token is stored before any kernel reads the cache.
+  st = pkv_append_kv(plan, k_new, v_new, kv_cache_layer, workspace, workspace_bytes, stream);
+  if (st != PKV_OK) return st;
+  return run_impl(plan, q, kv_cache_layer, out, lse, workspace, stream);
 }
 
 pkv_status pkv_append_kv(const pkv_plan* plan, const void* k_new, const void* v_new,

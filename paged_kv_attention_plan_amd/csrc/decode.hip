@@ -37,13 +37,18 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   const int tix = blockIdx.x * kWaves + wave;
   if (tix >= a.n_tiles) return;
 
-  const pkv_decode_tile* tp = a.tiles + tix;
-  const int hk = __builtin_amdgcn_readfirstlane(tp->kv_head);
-  const int ks = __builtin_amdgcn_readfirstlane(tp->kv_start);
-  const int ke = __builtin_amdgcn_readfirstlane(tp->kv_end);
-  const int page_base = __builtin_amdgcn_readfirstlane(tp->page_base);
-  const int q_index = __builtin_amdgcn_readfirstlane(tp->q_index);
-  const int out_slot = __builtin_amdgcn_readfirstlane(tp->out_slot);
+  // Plan metadata is read-only for the launch: scalar loads.
+  const auto tp = as_const4(a.tiles + tix);
+  const int row_ref = tp->row;
+  const int hk = tp->kv_head;
+  const int chunk = tp->chunk;
+  const int ks = tp->kv_start;
+  const int ke = tp->kv_end;
+  const auto rp = as_const4(a.rows + row_ref);
+  const int page_base = rp->page_base;
+  const int q_index = rp->q_index;
+  const int n_chunks = rp->n_chunks;
+  const int out_slot = rp->slot0 >= 0 ? rp->slot0 + hk * n_chunks + chunk : -1;
 
   const int Hq = a.num_qo_heads;
   const int Hk = a.num_kv_heads;
@@ -56,6 +61,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   const int lk = lane / LPK;   // key row within a load
   const int ld = lane % LPK;   // 8-element segment of head_dim
   const uint32_t lane_off = hk * D + ld * 8;
+  const_as4_ptr<int32_t> cidx = as_const4(a.indices);
 
   // Query heads hk*G .. hk*G+G-1, this lane's 8 dimensions, as packed bf16 pairs.
   uint32_t qw[G][4];
@@ -89,7 +95,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 
   // Physical page of block b (one page per block): a uniform load through the
   // scalar unit, fetched one block ahead of the loads that use it.
-  const_as4_ptr<int32_t> cidx = as_const4(a.indices);
   uint32_t lane_byte[U];  // byte offset of this lane's 16 bytes within a block
 #pragma unroll
   for (int u = 0; u < U; ++u) lane_byte[u] = ((u * KPL + lk) * (uint32_t)row_elems + lane_off) * 2u;
@@ -238,7 +243,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         pk.w = pack_bf16x2(o[h][6] * inv, o[h][7] * inv);
         *reinterpret_cast<uint4*>(a.out + ((int64_t)q_index * Hq + qh) * D + ld * 8) = pk;
         if (a.lse != nullptr && ld == 0) a.lse[(int64_t)q_index * Hq + qh] = lse_nat;
-      } else {
+      } else {  // split-KV partial, combined by the merge kernel
         float* po = a.part_o + ((int64_t)out_slot * G + h) * D + ld * 8;
         *reinterpret_cast<float4*>(po) = make_float4(o[h][0] * inv, o[h][1] * inv, o[h][2] * inv, o[h][3] * inv);
         *reinterpret_cast<float4*>(po + 4) = make_float4(o[h][4] * inv, o[h][5] * inv, o[h][6] * inv, o[h][7] * inv);

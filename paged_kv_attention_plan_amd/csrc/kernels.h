@@ -5,12 +5,14 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
+#include "meta.h"
 #include "pkv.h"
 
 namespace pkv {
 
 struct DecodeArgs {
-  const pkv_decode_tile* tiles;
+  const DecodeTileMeta* tiles;
+  const DecodeRowMeta* rows;
   int32_t n_tiles;
   const int32_t* indices;   // paged_kv_indices on the device
   const uint16_t* q;        // bf16 [total_q, Hq, D]

@@ -263,6 +263,18 @@ pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
     const int64_t n = kv_len[d.r];
     const int64_t nch = (d.vis + chunk - 1) / chunk;
     const int64_t base = slot;
+    if (nch > INT16_MAX) {
+      err = fmt_row("more than 32767 key chunks in one decode row", d.r);
+      return PKV_E_INVALID;
+    }
+    const int32_t row_ref = (int32_t)plan.decode_rows.size();
+    DecodeRowMeta rm{};
+    rm.page_base = kv_indptr[d.r];
+    rm.q_index = q_start[d.r];
+    rm.kv_len = (int32_t)n;
+    rm.slot0 = nch > 1 ? (int32_t)base : -1;
+    rm.n_chunks = (int32_t)nch;
+    plan.decode_rows.push_back(rm);
     for (int64_t i = 0; i < nch; ++i) {
       const int64_t p0 = d.fp + i * d.vis / nch, p1 = d.fp + (i + 1) * d.vis / nch;
       const int64_t ks = std::max(d.lo, p0 * ps);
@@ -278,6 +290,8 @@ pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
         t.out_slot = nch > 1 ? (int32_t)(base + hk * nch + i) : -1;
         t.kv_len = (int32_t)n;
         plan.decode_tiles.push_back(t);
+        plan.decode_tile_meta.push_back(
+            {row_ref, (int16_t)hk, (int16_t)i, (int32_t)ks, (int32_t)ke});
       }
     }
     if (nch > 1) {
@@ -333,8 +347,10 @@ pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
   // ---- workspace layout ----
   WorkspaceLayout& L = plan.ws;
   size_t off = kAlign;  // first 256 bytes reserved
+  L.off_decode_rows = off;
+  off = align_up(off + plan.decode_rows.size() * sizeof(DecodeRowMeta));
   L.off_decode_tiles = off;
-  off = align_up(off + plan.decode_tiles.size() * sizeof(pkv_decode_tile));
+  off = align_up(off + plan.decode_tile_meta.size() * sizeof(DecodeTileMeta));
   L.off_merges = off;
   off = align_up(off + plan.merges.size() * sizeof(pkv_merge_entry));
   L.off_prefill_tiles = off;
@@ -364,8 +380,10 @@ void serialize_meta(const PlanData& plan, void* dst) {
   auto put = [&](size_t off, const void* src, size_t bytes) {
     if (bytes) std::memcpy(base + off, src, bytes);
   };
-  put(plan.ws.off_decode_tiles, plan.decode_tiles.data(),
-      plan.decode_tiles.size() * sizeof(pkv_decode_tile));
+  put(plan.ws.off_decode_rows, plan.decode_rows.data(),
+      plan.decode_rows.size() * sizeof(DecodeRowMeta));
+  put(plan.ws.off_decode_tiles, plan.decode_tile_meta.data(),
+      plan.decode_tile_meta.size() * sizeof(DecodeTileMeta));
   put(plan.ws.off_merges, plan.merges.data(), plan.merges.size() * sizeof(pkv_merge_entry));
   put(plan.ws.off_prefill_tiles, plan.prefill_tiles.data(),
       plan.prefill_tiles.size() * sizeof(pkv_prefill_tile));

@@ -8,6 +8,7 @@
 #include <string>
 #include <vector>
 
+#include "meta.h"
 #include "pkv.h"
 
 namespace pkv {
@@ -16,8 +17,9 @@ namespace pkv {
 // regions [0, meta_bytes) are filled by the upload; the partial regions are
 // scratch written by split decode tiles and read by the merge.
 struct WorkspaceLayout {
-  size_t off_decode_tiles = 0;
-  size_t off_merges = 0;
+  size_t off_decode_rows = 0;     // DecodeRowMeta per decode row
+  size_t off_decode_tiles = 0;    // DecodeTileMeta per decode tile
+  size_t off_merges = 0;          // pkv_merge_entry per split (row, KV head)
   size_t off_prefill_tiles = 0;
   size_t off_indices = 0;
   size_t off_slots = 0;
@@ -38,7 +40,9 @@ struct PlanData {
   int32_t n_decode_rows = 0;
   int32_t n_prompt_rows = 0;
   std::vector<pkv_decode_tile> decode_tiles;
-  std::vector<pkv_merge_entry> merges;
+  std::vector<pkv_merge_entry> merges;         // every split (row, KV head)
+  std::vector<DecodeRowMeta> decode_rows;      // device form of the decode tiles
+  std::vector<DecodeTileMeta> decode_tile_meta;
   std::vector<pkv_prefill_tile> prefill_tiles;
   std::vector<int32_t> indices;  // copy of paged_kv_indices
   std::vector<int64_t> slots;    // flat write slot per query token

@@ -78,6 +78,8 @@ def _load():
                               C.c_void_p, C.c_size_t, C.c_void_p]),
         "pkv_append_kv": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.c_size_t, C.c_void_p]),
+        "pkv_run_append": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
         "pkv_timing_enable": (C.c_int, [C.c_void_p, C.c_int32]),
         "pkv_timing_read": (C.c_int, [C.c_void_p, P(C.c_double), P(C.c_int64)]),
         "pkv_last_error": (C.c_char_p, []),
@@ -94,7 +96,7 @@ _lib = _load()
 EXPORTED = ("pkv_plan_params_init", "pkv_plan_create", "pkv_plan_update", "pkv_plan_destroy",
             "pkv_plan_decode_tiles", "pkv_plan_prefill_tiles", "pkv_plan_merges",
             "pkv_plan_write_slots", "pkv_plan_permutation", "pkv_plan_info", "pkv_plan_upload",
-            "pkv_run", "pkv_append_kv", "pkv_timing_enable", "pkv_timing_read",
+            "pkv_run", "pkv_append_kv", "pkv_run_append", "pkv_timing_enable", "pkv_timing_read",
             "pkv_last_error", "pkv_version")
 
 
@@ -211,8 +213,10 @@ def plan_update(plan: Plan, qo_indptr, paged_kv_indptr, paged_kv_indices, paged_
 
 
 def _stream(stream):
+    """A hipStream_t for the C calls: a torch stream, a raw handle, or (None)
+    torch's current stream."""
     if stream is not None:
-        return C.c_void_p(int(stream))
+        return C.c_void_p(int(getattr(stream, "cuda_stream", stream)))
     import torch
     return C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -263,6 +267,20 @@ def run(plan: Plan, q, kv_cache_layer, out, workspace, lse=None, stream=None):
                         _dev(out, "out", torch.bfloat16), _dev(lse, "lse", torch.float32),
                         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                         _stream(stream)))
+
+
+def run_append(plan: Plan, q, k_new, v_new, kv_cache_layer, out, workspace, lse=None, stream=None):
+    """pkv_run_append: store this step's K/V, then run attention (append_kv
+    followed by run on one stream)."""
+    import torch
+    _check_sizes(plan, kv_cache_layer, q=q, out=out, lse=lse, k_new=k_new, v_new=v_new)
+    _check(_lib.pkv_run_append(plan.handle, _dev(q, "q", torch.bfloat16),
+                               _dev(k_new, "k_new", torch.bfloat16),
+                               _dev(v_new, "v_new", torch.bfloat16),
+                               _dev(kv_cache_layer, "kv_cache_layer", torch.bfloat16),
+                               _dev(out, "out", torch.bfloat16), _dev(lse, "lse", torch.float32),
+                               _dev(workspace, "workspace"),
+                               workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def append_kv(plan: Plan, k_new, v_new, kv_cache_layer, workspace, stream=None):

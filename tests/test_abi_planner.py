@@ -282,6 +282,18 @@ def test_error_run_before_upload():
     assert st == pkv.E_STATE
 
 
+def test_error_run_append_before_upload():
+    w = _tiny()
+    plan = pkv.plan_create(_params(w, "decode"), None, w.kv_indptr, w.kv_indices, w.last_page_len)
+    import ctypes
+    v = ctypes.c_void_p(4096)
+    st = pkv._lib.pkv_run_append(plan.handle, v, v, v, v, v, None, v, plan.ws_bytes,
+                                 ctypes.c_void_p(0))
+    assert st == pkv.E_STATE
+    st = pkv._lib.pkv_run_append(None, v, v, v, v, v, None, v, plan.ws_bytes, ctypes.c_void_p(0))
+    assert st == pkv.E_INVALID
+
+
 def test_plan_update_reuses_handle_and_keeps_old_plan_on_error():
     w = _tiny()
     p = _params(w, "decode")
