@@ -1,7 +1,7 @@
 """Benchmark: batched attention over a paged KV cache on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--config NAME] [--no-cpu-baseline]
-                    [--no-secondary]
+                    [--no-secondary] [--no-ceilings]
 
 A step is one pass of the whole hot path over one batch of synthetic input that
 is already resident in HBM: host re-plan of the page table (pkv_plan_update),
@@ -14,6 +14,12 @@ The headline workload is batched GQA decode with append: 128 requests,
 per second.  The other workloads (long-context split-KV decode, causal ragged
 prefill, mixed step with a sliding window) are measured briefly and reported
 under "secondary".
+
+Besides the contract fields the line carries, per kernel kind, the mean and
+p10 / median / p90 of the event-timed launch durations; the host time of
+pkv_plan_update and the device time of the metadata upload, measured apart
+from the step; and measured ceilings of this GPU (a 2 GiB device copy and a
+bf16 GEMM) as context for the spec peaks.
 
 Prints ONE JSON line.
 """
@@ -183,16 +189,89 @@ class Runner:
         return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
 
     def kernel_times(self, steps):
-        """Average per-launch ms of each kernel kind over `steps` steps, from HIP
-        events the library records around its launches on this stream."""
+        """Per-launch ms of each kernel kind over `steps` steps, from HIP events
+        the library records around its launches on this stream: kind -> list."""
         pkv = self.pkv
         pkv.timing_read(self.plan)  # clear
         pkv.timing_enable(self.plan, True)
+        per = {}
         for _ in range(steps):
             self.step()
-        res = pkv.timing_read(self.plan)
+            for k, (ms, n) in pkv.timing_read(self.plan).items():
+                if n:
+                    per.setdefault(k, []).append(ms / n)
         pkv.timing_enable(self.plan, False)
-        return {k: (ms / n if n else None, n) for k, (ms, n) in res.items()}
+        return {k: per.get(k, []) for k in ("append", "decode", "merge", "prefill")}
+
+    def host_times(self, steps):
+        """Host µs of plan_update and device µs of the metadata upload (events
+        around pkv_plan_upload on this stream), per step."""
+        w, pkv, torch = self.w, self.pkv, self.torch
+        plan_us, up_us = [], []
+        for _ in range(steps):
+            t0 = time.perf_counter()
+            pkv.plan_update(self.plan, self.qo, w.kv_indptr, w.kv_indices, w.last_page_len)
+            plan_us.append((time.perf_counter() - t0) * 1e6)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pkv.plan_upload(self.plan, self.ws)
+            e1.record()
+            e1.synchronize()
+            up_us.append(e0.elapsed_time(e1) * 1e3)
+        return {"plan_update_us": stats(plan_us), "upload_us": stats(up_us),
+                "upload_bytes": self.plan.info()["meta_bytes"]}
+
+
+def stats(xs, scale=1.0):
+    """mean / p10 / median / p90 of a list (None when empty), times scale."""
+    if not xs:
+        return None
+    a = np.sort(np.asarray(xs, dtype=np.float64)) * scale
+    q = lambda f: float(a[min(len(a) - 1, int(round(f * (len(a) - 1))))])
+    return {"mean": round(float(a.mean()), 2), "p10": round(q(0.1), 2),
+            "median": round(q(0.5), 2), "p90": round(q(0.9), 2), "n": int(len(a))}
+
+
+def mean_ms(xs):
+    return sum(xs) / len(xs) if xs else None
+
+
+def ceilings(dev):
+    """Measured ceilings on this GPU, for context beside the spec peaks: a
+    device-to-device copy of 2 GiB (bytes read + written per second) and a
+    bf16 8192^3 matrix product (torch / hipBLASLt), each the best of 5."""
+    import torch
+    n = 1 << 30  # bf16 elements: 2 GiB per buffer
+    src = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    best = []
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        best.append(e0.elapsed_time(e1))
+    copy_gbs = 2 * src.numel() * 2 / (min(best[1:]) * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device=dev).to(torch.bfloat16).contiguous()
+    b = torch.randn(m, m, device=dev).to(torch.bfloat16).contiguous()
+    best = []
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.mm(a, b)
+        e1.record()
+        e1.synchronize()
+        best.append(e0.elapsed_time(e1))
+    gemm_tfs = 2 * m ** 3 / (min(best[1:]) * 1e-3) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_GBps": round(copy_gbs, 1), "bf16_gemm_TFLOPs": round(gemm_tfs, 1),
+            "copy": "torch copy_ of 2 GiB, read + write bytes, best of 5",
+            "gemm": "torch.mm bf16 8192 x 8192 x 8192, best of 5"}
 
 
 def cpu_baseline(runner, unit, budget_s=12.0):
@@ -237,17 +316,18 @@ def secondary(name, dev, steps, warmup):
     r = Runner(name, dev)
     ms, _ = r.time_steps(steps, warmup)
     kt = r.kernel_times(steps)
-    res = {"workload": DESCR[name], "ms_per_step": round(ms, 4)}
+    res = {"workload": DESCR[name], "ms_per_step": round(ms, 4),
+           "kernels_us": {k: stats(v, 1e3) for k, v in kt.items() if v}}
     if r.work["kv_bytes"]:
-        dms = kt["decode"][0]
+        dms = mean_ms(kt["decode"])
         res["decode_kernel_us"] = round(dms * 1e3, 2)
         res["decode_kv_GBps_per_kernel"] = round(r.work["decode_bytes"] / (dms * 1e-3) / 1e9, 1)
         res["decode_frac_hbm_peak"] = round(res["decode_kv_GBps_per_kernel"] / HBM_PEAK_GBS, 4)
-        if kt["merge"][0] is not None:
-            res["merge_kernel_us"] = round(kt["merge"][0] * 1e3, 2)
+        if kt["merge"]:
+            res["merge_kernel_us"] = round(mean_ms(kt["merge"]) * 1e3, 2)
         res["kv_GBps_per_step"] = round(r.work["kv_bytes"] / (ms * 1e-3) / 1e9, 1)
     if r.work["prefill_flops"]:
-        pms = kt["prefill"][0]
+        pms = mean_ms(kt["prefill"])
         res["prefill_kernel_us"] = round(pms * 1e3, 2)
         res["prefill_TFLOPs_per_kernel"] = round(r.work["prefill_flops"] / (pms * 1e-3) / 1e12, 1)
         res["prefill_frac_mfma_peak"] = round(res["prefill_TFLOPs_per_kernel"] / MFMA_BF16_PEAK_TFS, 4)
@@ -265,6 +345,8 @@ def main():
     ap.add_argument("--config", default="gqa_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured copy / bf16 GEMM ceilings")
     ap.add_argument("--tiles-per-cu", type=int, default=0,
                     help="split-KV planner knob (0 = library default)")
     ap.add_argument("--min-chunk-pages", type=int, default=0,
@@ -277,8 +359,9 @@ def main():
         record_traffic(*args.record_traffic)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this path has no multi-GPU code "
-              "(see DESIGN.md for how it would shard).", file=sys.stderr)
+        print("bench.py runs on one GPU only: this path has no multi-GPU code; rows, KV "
+              "heads or a long row's pages would be split across GPUs, each running this "
+              "kernel on its share.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -291,7 +374,7 @@ def main():
     w = r.work
     if w["kv_bytes"]:  # decode rows present: KV bytes per second, decode kernel on HBM
         value, unit = w["kv_bytes"] / (ms * 1e-3) / 1e9, "GB/s"
-        dec_ms = kt["decode"][0]
+        dec_ms = mean_ms(kt["decode"])
         achieved = w["decode_bytes"] / (dec_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -300,7 +383,7 @@ def main():
                 "bytes_per_launch": w["decode_bytes"]}
     else:  # prefill only: FLOP per second, prefill kernel on bf16 MFMA
         value, unit = w["prefill_flops"] / (ms * 1e-3) / 1e12, "TFLOP/s"
-        pre_ms = kt["prefill"][0]
+        pre_ms = mean_ms(kt["prefill"])
         achieved = w["prefill_flops"] / (pre_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
@@ -325,9 +408,10 @@ def main():
                    "step": "plan_update + upload + append_kv + run (decode + split-KV merge)"
                    if r.append else "plan_update + upload + run"},
         "roofline": roof,
-        "kernels_us": {k: (round(v[0] * 1e3, 2) if v[0] is not None else None)
-                       for k, v in kt.items()},
+        "kernels_us": {k: (round(mean_ms(v) * 1e3, 2) if v else None) for k, v in kt.items()},
+        "kernels_us_dist": {k: stats(v, 1e3) for k, v in kt.items() if v},
         "host_ms_per_step": round(wall_ms, 4),
+        "host": r.host_times(args.steps),
         "plan": r.plan.info(),
     }
     if not args.no_secondary:
@@ -336,6 +420,8 @@ def main():
             if name != args.config:
                 sec.append(secondary(name, dev, max(5, args.steps // 5), 2))
         line["secondary"] = sec
+    if not args.no_ceilings:
+        line["measured_ceilings"] = ceilings(dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(r, unit)
     print(json.dumps(line), flush=True)

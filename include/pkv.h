@@ -181,11 +181,13 @@ pkv_status pkv_plan_permutation(const pkv_plan* plan, const int32_t** perm, int3
 pkv_status pkv_plan_info(const pkv_plan* plan, int64_t info[16]);
 
 /* Copy the plan's metadata into the head of `workspace` (device memory of at least
- * the plan's workspace_bytes) with hipMemcpyAsync on `stream` (a hipStream_t; NULL =
- * the null stream) from a page-locked staging buffer.  The staging buffer the copy
- * reads is reused only after that copy has completed (an event recorded behind it),
- * so re-planning while earlier steps are in flight is safe (attn.dense
- * force_double_buffer hazard).  PKV_E_WORKSPACE if workspace_bytes is too small. */
+ * the plan's workspace_bytes), enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream).  The metadata is serialised into a page-locked, host-coherent staging
+ * buffer and a small kernel on `stream` reads it over the host link into the
+ * workspace.  The staging buffer is rewritten only after the kernel that last read
+ * it has completed (an event recorded behind it), so re-planning while earlier steps
+ * are in flight is safe (attn.dense force_double_buffer hazard).  PKV_E_WORKSPACE if
+ * workspace_bytes is too small. */
 pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Attention for every planned query (FlashInfer*Wrapper.run analogue).

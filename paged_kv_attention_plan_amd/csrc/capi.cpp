@@ -32,6 +32,7 @@ pkv_status fail(pkv_status s, std::string msg) {
 // rewritten only after the copy that last read it has completed.
 struct Stage {
   void* host = nullptr;
+  void* dev = nullptr;  // the same memory as seen by the GPU
   size_t cap = 0;
   hipEvent_t ev = nullptr;
   bool pending = false;
@@ -245,16 +246,24 @@ pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_byt
   if (s.cap < meta) {
     if (s.host != nullptr) PKV_HIP(hipHostFree(s.host));
     s.host = nullptr;
+    s.dev = nullptr;
     s.cap = 0;
     size_t cap = 4096;
     while (cap < meta) cap <<= 1;
-    PKV_HIP(hipHostMalloc(&s.host, cap, hipHostMallocDefault));
+    // Coherent: the upload kernel reads it over the host link, never from a
+    // stale cache line of an earlier step.
+    PKV_HIP(hipHostMalloc(&s.host, cap, hipHostMallocCoherent));
     s.cap = cap;
+    PKV_HIP(hipHostGetDevicePointer(&s.dev, s.host, 0));
   }
   if (s.ev == nullptr) PKV_HIP(hipEventCreateWithFlags(&s.ev, hipEventDisableTiming));
   pkv::serialize_meta(plan->d, s.host);
   hipStream_t st_ = static_cast<hipStream_t>(stream);
-  PKV_HIP(hipMemcpyAsync(workspace, s.host, meta, hipMemcpyHostToDevice, st_));
+  pkv::UploadArgs ua{};
+  ua.src = static_cast<const uint4*>(s.dev);
+  ua.dst = static_cast<uint4*>(workspace);
+  ua.n_vec = (int64_t)(meta / 16);  // meta_bytes is a multiple of 256
+  PKV_HIP(pkv::launch_upload(ua, st_));
   PKV_HIP(hipEventRecord(s.ev, st_));
   s.pending = true;
   plan->next ^= 1;

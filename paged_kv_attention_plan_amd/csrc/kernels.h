@@ -57,6 +57,15 @@ struct PrefillArgs {
   float scale_log2;
 };
 
+// Plan metadata upload: the GPU copies n_vec 16-byte vectors from page-locked
+// host memory (device-visible pointer) into the workspace.
+struct UploadArgs {
+  const uint4* src;
+  uint4* dst;
+  int64_t n_vec;
+};
+
+hipError_t launch_upload(const UploadArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);

@@ -1,4 +1,4 @@
-// Split-KV merge and KV append.
+// Split-KV merge, KV append and the plan metadata upload.
 //
 // Merge (the workspace page, mstar attn.workspace, keeps split-KV partials):
 // a row whose keys were cut into chunks c has, per query head, a partial output
@@ -9,6 +9,11 @@
 // resource stores K/V before attention runs, attn.dense requires_kv_write):
 // token t's K row goes to cache[page, 0, off] and its V row to
 // cache[page, 1, off] with page * page_size + off = slot[t].
+//
+// Upload (kv.plan PinnedIndexRing stages the plan in page-locked memory): the
+// GPU reads the staged bytes over the host link and stores them into the
+// workspace.  For the tens to hundreds of KB of a plan this costs a few
+// microseconds, where a DMA copy pays its engine's start-up latency.
 #include "common.cuh"
 #include "kernels.h"
 
@@ -93,7 +98,23 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
+__global__ __launch_bounds__(256) void upload_kernel(UploadArgs a) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.n_vec; i += stride)
+    a.dst[i] = a.src[i];
+}
+
 }  // namespace
+
+hipError_t launch_upload(const UploadArgs& a, hipStream_t stream) {
+  if (a.n_vec <= 0) return hipSuccess;
+  // Every vector in flight at once up to 256 workgroups (1 MiB); larger
+  // plans loop.
+  int64_t blocks = (a.n_vec + 255) / 256;
+  blocks = blocks > 256 ? 256 : blocks;
+  hipLaunchKernelGGL(upload_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   if (a.n_merges <= 0) return hipSuccess;
