@@ -328,6 +328,7 @@ pkv_status run_impl(const pkv_plan* plan, const void* q, const void* kv_cache_la
     pkv::MergeArgs a{};
     a.merges = reinterpret_cast<const pkv_merge_entry*>(ws + d.ws.off_merges);
     a.n_merges = (int32_t)d.merges.size();
+    a.max_chunks = d.max_merge_chunks;
     a.part_o = part_o;
     a.part_lse = part_lse;
     a.out = static_cast<uint16_t*>(out);

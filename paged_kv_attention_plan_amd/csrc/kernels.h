@@ -28,6 +28,7 @@ struct DecodeArgs {
 struct MergeArgs {
   const pkv_merge_entry* merges;
   int32_t n_merges;
+  int32_t max_chunks;       // largest n_chunks of any entry
   const float* part_o;
   const float* part_lse;
   uint16_t* out;

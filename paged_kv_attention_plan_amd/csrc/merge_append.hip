@@ -22,52 +22,99 @@ namespace {
 
 constexpr int kWaves = 4;
 
-// One workgroup per (merge entry, query head).  The log-sum-exp of all chunks
-// is found first (every lane reads a strided subset of the chunk LSEs); then
-// each wave accumulates a quarter of the chunks with all of its loads
-// independent, and the four partial sums are added through LDS.
-template <int D>
+// Each (merge entry, query head) pair is merged by W waves (W = kWaves for
+// entries with many chunks, one wave otherwise, four pairs per workgroup).
+// A wave takes chunks c = w, w + W, ... in batches of U: lane i loads the LSE
+// of the batch's i-th chunk while every lane loads its slice of all U partial
+// outputs, so a batch costs one round trip to memory.  The wave keeps a
+// running maximum, so no pass over the LSEs precedes the sums.  With W > 1
+// the waves' (max, sum, acc) meet in LDS and are rescaled to the common
+// maximum there.
+template <int D, int W>
 __global__ __launch_bounds__(64 * kWaves) void merge_kernel(MergeArgs a) {
-  constexpr int E = D / 64;  // output elements per lane
+  constexpr int E = D / 64;          // output elements per lane
+  constexpr int U = W == 1 ? 8 : 16;  // chunks per batch
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = a.group;
-  const int mi = blockIdx.x / G, h = blockIdx.x - mi * G;
+  // pair index and this wave's rank among the pair's W waves
+  const int pair = W == 1 ? blockIdx.x * kWaves + wave : blockIdx.x;
+  const int rank = W == 1 ? 0 : wave;
+  if (pair >= a.n_merges * G) return;
+  const int mi = pair / G, h = pair - mi * G;
   const pkv_merge_entry e = a.merges[mi];
   const int n = e.n_chunks;
   const float* pl = a.part_lse + (int64_t)e.slot_base * G + h;
-  __shared__ float red[kWaves][D + 1];
-  __shared__ float s_max[kWaves];
-
-  float M = -INFINITY;
-  for (int c = threadIdx.x; c < n; c += 64 * kWaves) M = fmaxf(M, pl[(int64_t)c * G]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) s_max[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-
-  float wsum = 0.f, acc[E];
-#pragma unroll
-  for (int k = 0; k < E; ++k) acc[k] = 0.f;
   const float* po = a.part_o + ((int64_t)e.slot_base * G + h) * D + lane * E;
   const int64_t cstride = (int64_t)G * D;
-#pragma unroll 4
-  for (int c = wave; c < n; c += kWaves) {
-    const float wc = __expf(pl[(int64_t)c * G] - M);
-    wsum += wc;
+
+  float m_w = -INFINITY, wsum = 0.f, acc[E];
 #pragma unroll
-    for (int k = 0; k < E; ++k) acc[k] = fmaf(wc, po[c * cstride + k], acc[k]);
+  for (int k = 0; k < E; ++k) acc[k] = 0.f;
+  for (int c0 = rank; c0 < n; c0 += W * U) {
+    // lane i: LSE of chunk c0 + (i mod U) W (clamped; every lane loads, so the
+    // load is issued with the partials and not behind a branch)
+    const int cl = c0 + (lane & (U - 1)) * W;
+    const float lv = pl[(int64_t)(cl < n ? cl : n - 1) * G];
+    float o[U][E];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * W;
+      const int cc = c < n ? c : n - 1;  // in-range address; its weight is zero
+#pragma unroll
+      for (int k = 0; k < E; ++k) o[u][k] = po[cc * cstride + k];
+    }
+    float l[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      l[u] = c0 + u * W < n
+                 ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lv), u))
+                 : -INFINITY;
+    // chunk c0 exists, so mb and mn are finite
+    float mb = l[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) mb = fmaxf(mb, l[u]);
+    const float mn = fmaxf(m_w, mb);
+    const float sc = __expf(m_w - mn);
+    wsum *= sc;
+#pragma unroll
+    for (int k = 0; k < E; ++k) acc[k] *= sc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wc = __expf(l[u] - mn);
+      wsum += wc;
+#pragma unroll
+      for (int k = 0; k < E; ++k) acc[k] = fmaf(wc, o[u][k], acc[k]);
+    }
+    m_w = mn;
   }
+  float M = m_w, tot = wsum;
+  if constexpr (W > 1) {
+    __shared__ float red[W][D];
+    __shared__ float s_m[W], s_s[W];
 #pragma unroll
-  for (int k = 0; k < E; ++k) red[wave][lane * E + k] = acc[k];
-  if (lane == 0) red[wave][D] = wsum;
-  __syncthreads();
-  if (wave != 0) return;
-  float tot = red[0][D] + red[1][D] + red[2][D] + red[3][D];
+    for (int k = 0; k < E; ++k) red[wave][lane * E + k] = acc[k];
+    if (lane == 0) {
+      s_m[wave] = m_w;
+      s_s[wave] = wsum;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    M = s_m[0];
 #pragma unroll
-  for (int k = 0; k < E; ++k)
-    acc[k] = red[0][lane * E + k] + red[1][lane * E + k] + red[2][lane * E + k] + red[3][lane * E + k];
+    for (int w = 1; w < W; ++w) M = fmaxf(M, s_m[w]);
+    tot = 0.f;
+#pragma unroll
+    for (int k = 0; k < E; ++k) acc[k] = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      // a wave without chunks holds max -inf and contributes nothing
+      const float f = s_m[w] == -INFINITY ? 0.f : __expf(s_m[w] - M);
+      tot = fmaf(f, s_s[w], tot);
+#pragma unroll
+      for (int k = 0; k < E; ++k) acc[k] = fmaf(f, red[w][lane * E + k], acc[k]);
+    }
+  }
   const float inv = 1.f / tot;
   const int qh = e.kv_head * G + h;
   uint16_t* dst = a.out + ((int64_t)e.q_index * a.num_qo_heads + qh) * D + lane * E;
@@ -118,10 +165,21 @@ hipError_t launch_upload(const UploadArgs& a, hipStream_t stream) {
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   if (a.n_merges <= 0) return hipSuccess;
-  const dim3 grid(a.n_merges * a.group), block(64 * kWaves);
-  if (a.head_dim == 128) hipLaunchKernelGGL(merge_kernel<128>, grid, block, 0, stream, a);
-  else if (a.head_dim == 64) hipLaunchKernelGGL(merge_kernel<64>, grid, block, 0, stream, a);
-  else return hipErrorInvalidValue;
+  const int64_t pairs = (int64_t)a.n_merges * a.group;
+  const dim3 block(64 * kWaves);
+  // Entries of up to 8 chunks: one wave per pair, four pairs per workgroup.
+  // Longer ones: the four waves of a workgroup share a pair's chunks.
+  const bool wide = a.max_chunks > 8;
+  const dim3 grid(wide ? (unsigned)pairs : (unsigned)((pairs + kWaves - 1) / kWaves));
+  if (a.head_dim == 128) {
+    if (wide) hipLaunchKernelGGL((merge_kernel<128, kWaves>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((merge_kernel<128, 1>), grid, block, 0, stream, a);
+  } else if (a.head_dim == 64) {
+    if (wide) hipLaunchKernelGGL((merge_kernel<64, kWaves>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((merge_kernel<64, 1>), grid, block, 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -298,6 +298,7 @@ pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
       for (int32_t hk = 0; hk < Hk; ++hk)
         plan.merges.push_back({q_start[d.r], hk, (int32_t)(base + hk * nch), (int32_t)nch});
       slot += Hk * nch;
+      plan.max_merge_chunks = std::max(plan.max_merge_chunks, (int32_t)nch);
     }
   }
   if (slot > INT32_MAX) {

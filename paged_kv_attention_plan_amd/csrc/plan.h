@@ -37,6 +37,7 @@ struct PlanData {
   int32_t group = 1;
   int32_t chunk_pages = 0;
   int32_t n_slots = 0;
+  int32_t max_merge_chunks = 0;  // largest n_chunks over merges
   int32_t n_decode_rows = 0;
   int32_t n_prompt_rows = 0;
   std::vector<pkv_decode_tile> decode_tiles;
