@@ -58,8 +58,8 @@
  * Errors: every call returns a pkv_status; pkv_last_error() returns a message
  * for the calling thread's last failure (valid until that thread's next call).
  * Device work is enqueued on the given stream and is never synchronised by the
- * library, except that re-using a staging buffer waits for the copy that last
- * read it.
+ * library, except that re-using a staging buffer waits for the upload kernel that
+ * last read it.
  */
 #ifndef PKV_H_
 #define PKV_H_
@@ -184,10 +184,11 @@ pkv_status pkv_plan_info(const pkv_plan* plan, int64_t info[16]);
  * the plan's workspace_bytes), enqueued on `stream` (a hipStream_t; NULL = the null
  * stream).  The metadata is serialised into a page-locked, host-coherent staging
  * buffer and a small kernel on `stream` reads it over the host link into the
- * workspace.  The staging buffer is rewritten only after the kernel that last read
- * it has completed (an event recorded behind it), so re-planning while earlier steps
- * are in flight is safe (attn.dense force_double_buffer hazard).  PKV_E_WORKSPACE if
- * workspace_bytes is too small. */
+ * workspace.  The staging buffer is rewritten only after every workgroup of the
+ * kernel that last read it has flagged its reads done (a flag in the same
+ * host-coherent buffer), so re-planning while earlier steps are in flight is safe
+ * (attn.dense force_double_buffer hazard); this call waits for that, up to 60 s,
+ * then returns PKV_E_DEVICE.  PKV_E_WORKSPACE if workspace_bytes is too small. */
 pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Attention for every planned query (FlashInfer*Wrapper.run analogue).

@@ -2,8 +2,10 @@
 // upload, run and append.  Argument checks happen here, before any launch.
 #include <hip/hip_runtime.h>
 
+#include <chrono>
 #include <cmath>
 #include <cstring>
+#include <thread>
 #include <new>
 #include <string>
 #include <vector>
@@ -28,15 +30,46 @@ pkv_status fail(pkv_status s, std::string msg) {
       return fail(PKV_E_DEVICE, std::string(#expr) + " failed: " + hipGetErrorString(e_)); \
   } while (0)
 
-// One page-locked host buffer of the staging ring (kv.plan PinnedIndexRing):
-// rewritten only after the copy that last read it has completed.
+// One page-locked, host-coherent buffer of the staging ring (kv.plan
+// PinnedIndexRing): [0, cap) holds the serialised plan, followed by one
+// completion flag per upload workgroup.  Each workgroup of the upload kernel
+// that reads the buffer stores the upload's sequence number into its flag when
+// its reads are done, and the buffer is rewritten only after every flag holds
+// it.  (An event recorded behind the kernel would do the same, but costs the
+// stream a marker packet and several microseconds between kernels.)
+constexpr int kUploadBlocks = 256;  // most workgroups one upload launches
 struct Stage {
   void* host = nullptr;
   void* dev = nullptr;  // the same memory as seen by the GPU
   size_t cap = 0;
-  hipEvent_t ev = nullptr;
+  uint32_t seq = 0;     // sequence number of the last upload from this buffer
+  int n_flags = 0;      // workgroups of that upload
   bool pending = false;
+  volatile uint32_t* flags() const {
+    return reinterpret_cast<volatile uint32_t*>(static_cast<char*>(host) + cap);
+  }
 };
+
+// Wait until every workgroup of the stage's last upload has finished reading
+// it.  Spins (yielding) for up to 60 s; the GPU then counts as failed.
+bool wait_stage(Stage& s) {
+  if (!s.pending) return true;
+  const auto t0 = std::chrono::steady_clock::now();
+  for (int spin = 0;; ++spin) {
+    int i = 0;
+    while (i < s.n_flags && s.flags()[i] == s.seq) ++i;
+    if (i == s.n_flags) {
+      s.pending = false;
+      return true;
+    }
+    if (spin >= 64) {
+      std::this_thread::yield();
+      if ((spin & 1023) == 0 &&
+          std::chrono::steady_clock::now() - t0 > std::chrono::seconds(60))
+        return false;
+    }
+  }
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -162,9 +195,8 @@ void pkv_plan_destroy(pkv_plan* plan) {
   if (plan == nullptr) return;
   for (hipEvent_t e : plan->timing.pool) (void)hipEventDestroy(e);
   for (Stage& s : plan->stage) {
-    if (s.pending && s.ev != nullptr) (void)hipEventSynchronize(s.ev);
-    if (s.host != nullptr) (void)hipHostFree(s.host);
-    if (s.ev != nullptr) (void)hipEventDestroy(s.ev);
+    // A buffer the GPU may still read is not freed (it leaks if the GPU failed).
+    if (s.host != nullptr && wait_stage(s)) (void)hipHostFree(s.host);
   }
   delete plan;
 }
@@ -239,10 +271,8 @@ pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_byt
   if (st != PKV_OK) return st;
   const size_t meta = plan->d.ws.meta_bytes;
   Stage& s = plan->stage[plan->next];
-  if (s.pending) {
-    PKV_HIP(hipEventSynchronize(s.ev));
-    s.pending = false;
-  }
+  if (!wait_stage(s))
+    return fail(PKV_E_DEVICE, "a staging buffer's upload did not finish within 60 s");
   if (s.cap < meta) {
     if (s.host != nullptr) PKV_HIP(hipHostFree(s.host));
     s.host = nullptr;
@@ -251,20 +281,25 @@ pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_byt
     size_t cap = 4096;
     while (cap < meta) cap <<= 1;
     // Coherent: the upload kernel reads it over the host link, never from a
-    // stale cache line of an earlier step.
-    PKV_HIP(hipHostMalloc(&s.host, cap, hipHostMallocCoherent));
+    // stale cache line of an earlier step, and its flag stores reach the host.
+    PKV_HIP(hipHostMalloc(&s.host, cap + kUploadBlocks * sizeof(uint32_t), hipHostMallocCoherent));
     s.cap = cap;
     PKV_HIP(hipHostGetDevicePointer(&s.dev, s.host, 0));
+    for (int i = 0; i < kUploadBlocks; ++i) s.flags()[i] = s.seq;
   }
-  if (s.ev == nullptr) PKV_HIP(hipEventCreateWithFlags(&s.ev, hipEventDisableTiming));
   pkv::serialize_meta(plan->d, s.host);
   hipStream_t st_ = static_cast<hipStream_t>(stream);
   pkv::UploadArgs ua{};
   ua.src = static_cast<const uint4*>(s.dev);
   ua.dst = static_cast<uint4*>(workspace);
   ua.n_vec = (int64_t)(meta / 16);  // meta_bytes is a multiple of 256
-  PKV_HIP(pkv::launch_upload(ua, st_));
-  PKV_HIP(hipEventRecord(s.ev, st_));
+  ua.flags = reinterpret_cast<uint32_t*>(static_cast<char*>(s.dev) + s.cap);
+  ua.seq = s.seq + 1;
+  ua.max_blocks = kUploadBlocks;
+  int blocks = 0;
+  PKV_HIP(pkv::launch_upload(ua, st_, &blocks));
+  s.seq = ua.seq;
+  s.n_flags = blocks;
   s.pending = true;
   plan->next ^= 1;
   plan->uploaded_ws = workspace;

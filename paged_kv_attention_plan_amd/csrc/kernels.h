@@ -59,14 +59,19 @@ struct PrefillArgs {
 };
 
 // Plan metadata upload: the GPU copies n_vec 16-byte vectors from page-locked
-// host memory (device-visible pointer) into the workspace.
+// host memory (device-visible pointer) into the workspace.  Workgroup b then
+// stores seq into flags[b] (host-coherent memory) to mark its reads done.
 struct UploadArgs {
   const uint4* src;
   uint4* dst;
   int64_t n_vec;
+  uint32_t* flags;
+  uint32_t seq;
+  int32_t max_blocks;
 };
 
-hipError_t launch_upload(const UploadArgs& a, hipStream_t stream);
+// *blocks receives the number of workgroups launched (<= a.max_blocks).
+hipError_t launch_upload(const UploadArgs& a, hipStream_t stream, int* blocks);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);

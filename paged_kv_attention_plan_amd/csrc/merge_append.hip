@@ -127,39 +127,59 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(MergeArgs a) {
     a.lse[(int64_t)e.q_index * a.num_qo_heads + qh] = M + logf(tot);
 }
 
+// One workgroup per token.  The token's K and V vectors are requested before
+// the slot is needed, so the slot load and the data loads share one round
+// trip; page_size is a power of two, so the slot splits by shift and mask.
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int t = blockIdx.x;
   const int64_t slot = a.slots[t];
   const int ps = a.page_size;
-  const int64_t page = slot / ps;
-  const int off = (int)(slot - page * ps);
+  const int ps_log2 = __builtin_ctz(ps);
   const int row = a.num_kv_heads * a.head_dim;  // elements per token slot
   const int nvec = row / 8;                     // 16-byte vectors per row
-  uint16_t* dk = a.cache + ((page * 2 + 0) * ps + off) * (int64_t)row;
-  uint16_t* dv = dk + (int64_t)ps * row;
   const uint4* sk = reinterpret_cast<const uint4*>(a.k_new + (int64_t)t * row);
   const uint4* sv = reinterpret_cast<const uint4*>(a.v_new + (int64_t)t * row);
-  for (int i = threadIdx.x; i < 2 * nvec; i += blockDim.x) {
-    if (i < nvec) reinterpret_cast<uint4*>(dk)[i] = sk[i];
-    else reinterpret_cast<uint4*>(dv)[i - nvec] = sv[i - nvec];
+  auto store = [&](int i, const uint4& v) {
+    const int64_t page = slot >> ps_log2;
+    const int off = (int)(slot & (ps - 1));
+    uint16_t* dk = a.cache + ((page * 2 + 0) * ps + off) * (int64_t)row;
+    uint16_t* dst = i < nvec ? dk : dk + (int64_t)ps * row;
+    reinterpret_cast<uint4*>(dst)[i < nvec ? i : i - nvec] = v;
+  };
+  // The first vector of each thread (all of them when 2 nvec <= blockDim) is
+  // loaded before any use of the slot.
+  const int i0 = threadIdx.x;
+  if (i0 < 2 * nvec) {
+    const uint4 v = i0 < nvec ? sk[i0] : sv[i0 - nvec];
+    // keep the slot arithmetic (and its wait) behind the load's issue
+    __builtin_amdgcn_sched_barrier(0);
+    store(i0, v);
   }
+  for (int i = i0 + blockDim.x; i < 2 * nvec; i += blockDim.x) store(i, i < nvec ? sk[i] : sv[i - nvec]);
 }
 
 __global__ __launch_bounds__(256) void upload_kernel(UploadArgs a) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.n_vec; i += stride)
     a.dst[i] = a.src[i];
+  // Every thread's loads have returned (their data is stored): the host may
+  // rewrite this workgroup's share of the staging buffer.
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.flags + blockIdx.x, a.seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 }  // namespace
 
-hipError_t launch_upload(const UploadArgs& a, hipStream_t stream) {
+hipError_t launch_upload(const UploadArgs& a, hipStream_t stream, int* blocks) {
+  *blocks = 0;
   if (a.n_vec <= 0) return hipSuccess;
-  // Every vector in flight at once up to 256 workgroups (1 MiB); larger
-  // plans loop.
-  int64_t blocks = (a.n_vec + 255) / 256;
-  blocks = blocks > 256 ? 256 : blocks;
-  hipLaunchKernelGGL(upload_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  // Every vector in flight at once up to max_blocks workgroups; larger plans
+  // loop.
+  int64_t nb = (a.n_vec + 255) / 256;
+  nb = nb > a.max_blocks ? a.max_blocks : nb;
+  hipLaunchKernelGGL(upload_kernel, dim3((unsigned)nb), dim3(256), 0, stream, a);
+  *blocks = (int)nb;
   return hipGetLastError();
 }
 
