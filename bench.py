@@ -59,6 +59,9 @@ DESCR = {
                       "Hq 32 / Hk 8, D 128, page 16",
     "mixed_window": "mixed step, window 4096: 256 decode rows (kv_len U[256,8192]) + 4 prompt rows "
                     "(1024 on 2048 prefix), Hq 16 / Hk 16, D 64, page 32",
+    "gqa_decode_context_only": "context-only decode over the gqa_decode rows: each row's appended "
+                               "token dropped by context_only_views, one query per row attending "
+                               "to the stored kv_len - 1 keys",
 }
 
 
@@ -141,7 +144,17 @@ class Runner:
         from paged_kv_attention_plan_amd import pkv
         self.torch, self.pkv = torch, pkv
         self.name = name
-        self.w = synth.make_workload(name, device=dev)
+        self.context_only = name.endswith("_context_only")
+        self.w = synth.make_workload(name[:-len("_context_only")] if self.context_only else name,
+                                     device=dev)
+        if self.context_only:  # every row's last token is this step's
+            import dataclasses
+            w0 = self.w
+            self.views_in = (w0.page_size, w0.kv_indptr, w0.kv_indices, w0.last_page_len,
+                             np.ones(w0.batch, np.int32), np.ones(w0.batch, np.int32))
+            ptr, idx, lpl, _ = pkv.context_only_views(*self.views_in)
+            self.w = dataclasses.replace(w0, kv_len=w0.kv_len - 1, kv_indptr=ptr, kv_indices=idx,
+                                         last_page_len=lpl, causal=False)
         w = self.w
         if w.k_new is None and w.kind == "decode":
             g = torch.Generator(device=dev).manual_seed(7)
@@ -162,11 +175,19 @@ class Runner:
         self.out = torch.empty_like(w.q)
         self.lse = torch.empty(w.total_q, w.num_qo_heads, dtype=torch.float32, device=dev)
         self.append = w.kind == "decode" and name == "gqa_decode"
+        self.step_descr = ("context_only_views + plan_update + upload + run (decode + split-KV "
+                           "merge)" if self.context_only else
+                           "plan_update + upload + append_kv + run (decode + split-KV merge)"
+                           if self.append else "plan_update + upload + run")
         self.work = work_of(w)
 
     def step(self):
         w, pkv = self.w, self.pkv
-        pkv.plan_update(self.plan, self.qo, w.kv_indptr, w.kv_indices, w.last_page_len)
+        if self.context_only:  # the views are re-derived every step, as a serving loop would
+            ptr, idx, lpl, _ = pkv.context_only_views(*self.views_in)
+            pkv.plan_update(self.plan, self.qo, ptr, idx, lpl)
+        else:
+            pkv.plan_update(self.plan, self.qo, w.kv_indptr, w.kv_indices, w.last_page_len)
         pkv.plan_upload(self.plan, self.ws)
         if self.append:
             pkv.append_kv(self.plan, w.k_new, w.v_new, w.cache, self.ws)
@@ -405,8 +426,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": DESCR[args.config], "kv_bytes_per_step": w["kv_bytes"],
                    "prefill_flops_per_step": w["prefill_flops"],
-                   "step": "plan_update + upload + append_kv + run (decode + split-KV merge)"
-                   if r.append else "plan_update + upload + run"},
+                   "step": r.step_descr},
         "roofline": roof,
         "kernels_us": {k: (round(mean_ms(v) * 1e3, 2) if v else None) for k, v in kt.items()},
         "kernels_us_dist": {k: stats(v, 1e3) for k, v in kt.items() if v},
@@ -416,7 +436,7 @@ def main():
     }
     if not args.no_secondary:
         sec = []
-        for name in ("long_decode", "ragged_prefill", "mixed_window"):
+        for name in ("long_decode", "ragged_prefill", "mixed_window", "gqa_decode_context_only"):
             if name != args.config:
                 sec.append(secondary(name, dev, max(5, args.steps // 5), 2))
         line["secondary"] = sec

@@ -217,6 +217,30 @@ pkv_status pkv_append_kv(const pkv_plan* plan, const void* k_new, const void* v_
                          void* kv_cache_layer, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* The page table of a step's rows without the tokens the step appends
+ * (kv.plan context_only_views, for attention over the stored context alone).
+ * Row r of the input table (paged_kv_indptr / _indices / _last_page_len, the same
+ * CSR arrays pkv_plan_create takes, page_size a power of two in [1, 256]) holds
+ * kv_len_r tokens, the last to_compute[r] of them appended this step.  The output
+ * row keeps the first kv_len_r - to_compute[r] tokens: its pages are the first
+ * ceil(kept / page_size) of the input row's, its last_page_len follows from kept,
+ * and out_qo_indptr gives it query_spans[r] query tokens.
+ * Plan the result with causal = 0 so that every query sees every kept key (the
+ * kept tokens all precede the step's tokens); a row's query count must then
+ * still not exceed its kept length.
+ * Host only: no device call.  The caller allocates out_indptr[batch + 1],
+ * out_indices (at least as many entries as paged_kv_indices), out_last_page_len[batch]
+ * and out_qo_indptr[batch + 1].  Errors: PKV_E_INVALID for a malformed table,
+ * to_compute[r] outside [0, kv_len_r) (every row keeps a stored token) or a negative
+ * query_spans[r]; PKV_E_UNSUPPORTED for a bad page_size.  The outputs are partly
+ * written on error. */
+pkv_status pkv_context_only_views(int32_t batch, int32_t page_size, const int32_t* paged_kv_indptr,
+                                  const int32_t* paged_kv_indices,
+                                  const int32_t* paged_kv_last_page_len, const int32_t* to_compute,
+                                  const int32_t* query_spans, int32_t* out_indptr,
+                                  int32_t* out_indices, int32_t* out_last_page_len,
+                                  int32_t* out_qo_indptr);
+
 /* Per-launch timing, a tracing aid (the wrappers' enable_nvtx flag is the pages'
  * counterpart).  While enabled, pkv_run, pkv_run_append and pkv_append_kv record a HIP event on the
  * stream before and after every kernel they launch with this plan.

@@ -18,7 +18,7 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "RowLayout", "decode_csr", "query_position", "visible_keys",
     "kv_head_of", "gather_row_kv", "attention", "attention_rows", "attention_bruteforce", "write_slots",
-    "apply_append", "mixed_permutation", "merge_partials", "OracleError",
+    "apply_append", "mixed_permutation", "merge_partials", "context_only_views", "OracleError",
 ]
 
 
@@ -307,6 +307,39 @@ def apply_append(cache_bits: np.ndarray, slots, k_new_bits: np.ndarray, v_new_bi
         out[page, 0, off] = k_new_bits[t]
         out[page, 1, off] = v_new_bits[t]
     return out
+
+
+def context_only_views(page_size, kv_indptr, kv_indices, last_page_len, to_compute, query_spans):
+    """The page table of a step's rows without the tokens the step appends
+    (kv.plan, context_only_views): row r keeps its first
+    kv_len - to_compute[r] tokens, the pages past them are dropped, and its
+    query count becomes query_spans[r].  Every row must keep at least one
+    stored token (0 <= to_compute < kv_len) and query_spans[r] >= 0.
+    Returns (kv_indptr, kv_indices, last_page_len, qo_indptr) of the new views.
+    """
+    indptr = np.asarray(kv_indptr, dtype=np.int64)
+    indices = np.asarray(kv_indices, dtype=np.int64)
+    lpl = np.asarray(last_page_len, dtype=np.int64)
+    B = len(lpl)
+    new_ptr, new_idx, new_lpl, qo = [0], [], [], [0]
+    for r in range(B):
+        pages = indices[indptr[r]:indptr[r + 1]]
+        if len(pages) < 1 or not (1 <= lpl[r] <= page_size):
+            raise OracleError(f"row {r}: malformed page table")
+        kv_len = (len(pages) - 1) * page_size + int(lpl[r])
+        tc, qs = int(to_compute[r]), int(query_spans[r])
+        if not (0 <= tc < kv_len):
+            raise OracleError(f"row {r}: to_compute {tc} must lie in [0, kv_len={kv_len})")
+        if qs < 0:
+            raise OracleError(f"row {r}: query_spans {qs} < 0")
+        kept = kv_len - tc
+        n_pages = -(-kept // page_size)
+        new_idx.extend(int(p) for p in pages[:n_pages])
+        new_ptr.append(new_ptr[-1] + n_pages)
+        new_lpl.append(kept - (n_pages - 1) * page_size)
+        qo.append(qo[-1] + qs)
+    as32 = lambda a: np.asarray(a, dtype=np.int32)
+    return as32(new_ptr), as32(new_idx), as32(new_lpl), as32(qo)
 
 
 def mixed_permutation(qo_indptr, *, max_prefill_rows):

@@ -456,6 +456,22 @@ pkv_status pkv_append_kv(const pkv_plan* plan, const void* k_new, const void* v_
   return PKV_OK;
 }
 
+pkv_status pkv_context_only_views(int32_t batch, int32_t page_size, const int32_t* paged_kv_indptr,
+                                  const int32_t* paged_kv_indices,
+                                  const int32_t* paged_kv_last_page_len, const int32_t* to_compute,
+                                  const int32_t* query_spans, int32_t* out_indptr,
+                                  int32_t* out_indices, int32_t* out_last_page_len,
+                                  int32_t* out_qo_indptr) {
+  g_err.clear();
+  std::string err;
+  pkv_status st = pkv::context_only_views(batch, page_size, paged_kv_indptr, paged_kv_indices,
+                                          paged_kv_last_page_len, to_compute, query_spans,
+                                          out_indptr, out_indices, out_last_page_len,
+                                          out_qo_indptr, err);
+  if (st != PKV_OK) return fail(st, err);
+  return PKV_OK;
+}
+
 pkv_status pkv_timing_enable(pkv_plan* plan, int32_t enable) {
   g_err.clear();
   if (plan == nullptr) return fail(PKV_E_INVALID, "plan must not be NULL");

@@ -392,4 +392,71 @@ void serialize_meta(const PlanData& plan, void* dst) {
   put(plan.ws.off_slots, plan.slots.data(), plan.slots.size() * sizeof(int64_t));
 }
 
+// kv.plan context_only_views: each row keeps its first kv_len - to_compute
+// tokens (the pages past them dropped) and gets query_spans[r] queries.
+pkv_status context_only_views(int32_t batch, int32_t page_size, const int32_t* kv_indptr,
+                              const int32_t* kv_indices, const int32_t* last_page_len,
+                              const int32_t* to_compute, const int32_t* query_spans,
+                              int32_t* out_indptr, int32_t* out_indices,
+                              int32_t* out_last_page_len, int32_t* out_qo_indptr,
+                              std::string& err) {
+  if (batch < 0) {
+    err = "batch must be >= 0";
+    return PKV_E_INVALID;
+  }
+  if (!is_pow2(page_size) || page_size > 256) {
+    err = "page_size must be a power of two in [1, 256] (got " + std::to_string(page_size) + ")";
+    return PKV_E_UNSUPPORTED;
+  }
+  if (kv_indptr == nullptr || out_indptr == nullptr || out_qo_indptr == nullptr ||
+      (batch > 0 && (kv_indices == nullptr || last_page_len == nullptr || to_compute == nullptr ||
+                     query_spans == nullptr || out_indices == nullptr ||
+                     out_last_page_len == nullptr))) {
+    err = "NULL array";
+    return PKV_E_INVALID;
+  }
+  if (kv_indptr[0] != 0) {
+    err = "paged_kv_indptr[0] must be 0";
+    return PKV_E_INVALID;
+  }
+  out_indptr[0] = 0;
+  out_qo_indptr[0] = 0;
+  int64_t nnz = 0, nq = 0;
+  for (int32_t r = 0; r < batch; ++r) {
+    const int64_t np = (int64_t)kv_indptr[r + 1] - kv_indptr[r];
+    if (np < 1) {
+      err = fmt_row("every row needs at least one page", r);
+      return PKV_E_INVALID;
+    }
+    const int32_t lpl = last_page_len[r];
+    if (lpl < 1 || lpl > page_size) {
+      err = fmt_row("paged_kv_last_page_len must be in [1, page_size]", r);
+      return PKV_E_INVALID;
+    }
+    const int64_t n = (np - 1) * page_size + lpl;
+    const int64_t tc = to_compute[r], qs = query_spans[r];
+    if (tc < 0 || tc >= n) {
+      err = fmt_row("to_compute must be in [0, kv_len): a row keeps at least one stored token", r);
+      return PKV_E_INVALID;
+    }
+    if (qs < 0) {
+      err = fmt_row("query_spans must be >= 0", r);
+      return PKV_E_INVALID;
+    }
+    const int64_t kept = n - tc;
+    const int64_t kp = (kept + page_size - 1) / page_size;
+    for (int64_t i = 0; i < kp; ++i) out_indices[nnz + i] = kv_indices[kv_indptr[r] + i];
+    nnz += kp;
+    nq += qs;
+    if (nq > INT32_MAX) {
+      err = "more than 2^31 - 1 query tokens";
+      return PKV_E_INVALID;
+    }
+    out_indptr[r + 1] = (int32_t)nnz;
+    out_last_page_len[r] = (int32_t)(kept - (kp - 1) * page_size);
+    out_qo_indptr[r + 1] = (int32_t)nq;
+  }
+  return PKV_OK;
+}
+
 }  // namespace pkv

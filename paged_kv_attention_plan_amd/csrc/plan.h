@@ -64,4 +64,13 @@ pkv_status check_params(const pkv_plan_params& p, std::string& err);
 // Copy the metadata regions of `plan` into `dst` (meta_bytes bytes).
 void serialize_meta(const PlanData& plan, void* dst);
 
+// Page table of the rows without the step's appended tokens (see
+// pkv_context_only_views).
+pkv_status context_only_views(int32_t batch, int32_t page_size, const int32_t* kv_indptr,
+                              const int32_t* kv_indices, const int32_t* last_page_len,
+                              const int32_t* to_compute, const int32_t* query_spans,
+                              int32_t* out_indptr, int32_t* out_indices,
+                              int32_t* out_last_page_len, int32_t* out_qo_indptr,
+                              std::string& err);
+
 }  // namespace pkv

@@ -80,6 +80,7 @@ def _load():
                                     C.c_size_t, C.c_void_p]),
         "pkv_run_append": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+        "pkv_context_only_views": (C.c_int, [C.c_int32, C.c_int32] + [P(C.c_int32)] * 9),
         "pkv_timing_enable": (C.c_int, [C.c_void_p, C.c_int32]),
         "pkv_timing_read": (C.c_int, [C.c_void_p, P(C.c_double), P(C.c_int64)]),
         "pkv_last_error": (C.c_char_p, []),
@@ -96,7 +97,8 @@ _lib = _load()
 EXPORTED = ("pkv_plan_params_init", "pkv_plan_create", "pkv_plan_update", "pkv_plan_destroy",
             "pkv_plan_decode_tiles", "pkv_plan_prefill_tiles", "pkv_plan_merges",
             "pkv_plan_write_slots", "pkv_plan_permutation", "pkv_plan_info", "pkv_plan_upload",
-            "pkv_run", "pkv_append_kv", "pkv_run_append", "pkv_timing_enable", "pkv_timing_read",
+            "pkv_run", "pkv_append_kv", "pkv_run_append", "pkv_context_only_views",
+            "pkv_timing_enable", "pkv_timing_read",
             "pkv_last_error", "pkv_version")
 
 
@@ -295,6 +297,27 @@ def append_kv(plan: Plan, k_new, v_new, kv_cache_layer, workspace, stream=None):
 
 
 TIMING_KINDS = ("append", "decode", "merge", "prefill")
+
+
+def context_only_views(page_size, paged_kv_indptr, paged_kv_indices, paged_kv_last_page_len,
+                       to_compute, query_spans):
+    """pkv_context_only_views: the page table without the step's appended
+    tokens.  Returns (paged_kv_indptr, paged_kv_indices, paged_kv_last_page_len,
+    qo_indptr) as int32 arrays; plan them with causal=False."""
+    ind, idx, lpl, tc, qs = map(_i32, (paged_kv_indptr, paged_kv_indices, paged_kv_last_page_len,
+                                       to_compute, query_spans))
+    batch = len(lpl)
+    o_ind = np.zeros(batch + 1, dtype=np.int32)
+    o_idx = np.zeros(max(len(idx), 1), dtype=np.int32)
+    o_lpl = np.zeros(max(batch, 1), dtype=np.int32)
+    o_qo = np.zeros(batch + 1, dtype=np.int32)
+    if len(ind) != batch + 1 or len(tc) != batch or len(qs) != batch:
+        raise PkvError(1, "paged_kv_indptr needs batch + 1 entries and to_compute / query_spans "
+                          "batch entries")
+    _check(_lib.pkv_context_only_views(batch, int(page_size), _ptr(ind), _ptr(idx), _ptr(lpl),
+                                       _ptr(tc), _ptr(qs), _ptr(o_ind), _ptr(o_idx), _ptr(o_lpl),
+                                       _ptr(o_qo)))
+    return o_ind, o_idx[:o_ind[-1]].copy(), o_lpl[:batch].copy(), o_qo
 
 
 def timing_enable(plan: Plan, enable: bool = True):
