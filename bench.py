@@ -62,6 +62,9 @@ DESCR = {
     "gqa_decode_context_only": "context-only decode over the gqa_decode rows: each row's appended "
                                "token dropped by context_only_views, one query per row attending "
                                "to the stored kv_len - 1 keys",
+    "ragged_prefill_dense": "dense [prefix | fresh] mode over the ragged_prefill rows: prefixes "
+                            "gathered from the pages once, each step's fresh K/V copied after "
+                            "them, one dense varlen pass (contiguous K/V)",
 }
 
 
@@ -144,6 +147,9 @@ class Runner:
         from paged_kv_attention_plan_amd import pkv
         self.torch, self.pkv = torch, pkv
         self.name = name
+        self.dense = name.endswith("_dense")
+        if self.dense:
+            name = name[:-len("_dense")]
         self.context_only = name.endswith("_context_only")
         self.w = synth.make_workload(name[:-len("_context_only")] if self.context_only else name,
                                      device=dev)
@@ -162,6 +168,9 @@ class Runner:
             w.k_new = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
             w.v_new = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
         self.qo = None if w.kind == "decode" else w.qo_indptr
+        if self.dense:
+            self._init_dense(dev)
+            return
         self.params = pkv.plan_params(w.kind, num_qo_heads=w.num_qo_heads,
                                       num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
                                       page_size=w.page_size, max_pages=w.max_pages,
@@ -181,8 +190,67 @@ class Runner:
                            if self.append else "plan_update + upload + run")
         self.work = work_of(w)
 
+    def _init_dense(self, dev):
+        """Dense plan over the same rows: row r's prefix is its first
+        kv_len - q_len tokens; the step's fresh K/V are the rows' last q_len
+        tokens as the pool holds them.  The prefixes are gathered once here."""
+        torch, pkv, w = self.torch, self.pkv, self.w
+        self.cu_q = w.qo_indptr.astype(np.int32)
+        self.cu_k = np.concatenate([[0], np.cumsum(w.kv_len)]).astype(np.int32)
+        self.params = pkv.plan_params("dense", num_qo_heads=w.num_qo_heads,
+                                      num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                                      page_size=w.page_size, max_pages=w.max_pages,
+                                      causal=w.causal, window_left=w.window_left)
+        self.plan = pkv.dense_plan_create(self.params, self.cu_q, self.cu_k, w.kv_indptr,
+                                          w.kv_indices)
+        self.ws = torch.empty(self.plan.ws_bytes, dtype=torch.uint8, device=dev)
+        flat = []
+        for r in range(w.batch):
+            n, L = int(w.kv_len[r]), int(w.q_len[r])
+            for j in range(n - L, n):
+                flat.append(int(w.kv_indices[w.kv_indptr[r] + j // w.page_size]) * w.page_size
+                            + j % w.page_size)
+        idx = torch.tensor(flat, dtype=torch.int64, device=dev)
+        hk, d = w.num_kv_heads, w.head_dim
+        self.k_fresh = w.cache[:, 0].reshape(-1, hk, d)[idx].contiguous()
+        self.v_fresh = w.cache[:, 1].reshape(-1, hk, d)[idx].contiguous()
+        K = int(self.cu_k[-1])
+        self.k_dense = torch.empty(K, hk, d, dtype=torch.bfloat16, device=dev)
+        self.v_dense = torch.empty_like(self.k_dense)
+        pkv.plan_upload(self.plan, self.ws)
+        pkv.dense_gather(self.plan, w.cache, self.k_fresh, self.v_fresh, self.k_dense,
+                         self.v_dense, self.ws, with_prefix=True)
+        self.out = torch.empty_like(w.q)
+        self.lse = torch.empty(w.total_q, w.num_qo_heads, dtype=torch.float32, device=dev)
+        self.append = False
+        self.step_descr = ("dense_plan_update + upload + dense_gather (fresh rows) + dense_run; "
+                           "prefixes gathered once before the timed steps")
+        self.work = work_of(w)
+
+    def gather_prefix_us(self, reps=10):
+        """Event-timed µs of one full gather (prefixes from the pages + fresh rows)."""
+        pkv, torch = self.pkv, self.torch
+        pkv.timing_read(self.plan)
+        pkv.timing_enable(self.plan, True)
+        ts = []
+        for _ in range(reps):
+            pkv.dense_gather(self.plan, self.w.cache, self.k_fresh, self.v_fresh, self.k_dense,
+                             self.v_dense, self.ws, with_prefix=True)
+            ms, n = pkv.timing_read(self.plan)["append"]
+            ts.append(ms / n * 1e3)
+        pkv.timing_enable(self.plan, False)
+        return stats(ts)
+
     def step(self):
         w, pkv = self.w, self.pkv
+        if self.dense:
+            pkv.dense_plan_update(self.plan, self.cu_q, self.cu_k, w.kv_indptr, w.kv_indices)
+            pkv.plan_upload(self.plan, self.ws)
+            pkv.dense_gather(self.plan, None, self.k_fresh, self.v_fresh, self.k_dense,
+                             self.v_dense, self.ws, with_prefix=False)
+            pkv.dense_run(self.plan, w.q, self.k_dense, self.v_dense, self.out, self.ws,
+                          lse=self.lse)
+            return
         if self.context_only:  # the views are re-derived every step, as a serving loop would
             ptr, idx, lpl, _ = pkv.context_only_views(*self.views_in)
             pkv.plan_update(self.plan, self.qo, ptr, idx, lpl)
@@ -231,7 +299,10 @@ class Runner:
         plan_us, up_us = [], []
         for _ in range(steps):
             t0 = time.perf_counter()
-            pkv.plan_update(self.plan, self.qo, w.kv_indptr, w.kv_indices, w.last_page_len)
+            if self.dense:
+                pkv.dense_plan_update(self.plan, self.cu_q, self.cu_k, w.kv_indptr, w.kv_indices)
+            else:
+                pkv.plan_update(self.plan, self.qo, w.kv_indptr, w.kv_indices, w.last_page_len)
             plan_us.append((time.perf_counter() - t0) * 1e6)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -347,6 +418,9 @@ def secondary(name, dev, steps, warmup):
         if kt["merge"]:
             res["merge_kernel_us"] = round(mean_ms(kt["merge"]) * 1e3, 2)
         res["kv_GBps_per_step"] = round(r.work["kv_bytes"] / (ms * 1e-3) / 1e9, 1)
+    if r.dense:
+        res["gather_fresh_us"] = round(mean_ms(kt["append"]) * 1e3, 2)
+        res["gather_with_prefix_us"] = r.gather_prefix_us()
     if r.work["prefill_flops"]:
         pms = mean_ms(kt["prefill"])
         res["prefill_kernel_us"] = round(pms * 1e3, 2)
@@ -436,7 +510,8 @@ def main():
     }
     if not args.no_secondary:
         sec = []
-        for name in ("long_decode", "ragged_prefill", "mixed_window", "gqa_decode_context_only"):
+        for name in ("long_decode", "ragged_prefill", "mixed_window", "gqa_decode_context_only",
+                     "ragged_prefill_dense"):
             if name != args.config:
                 sec.append(secondary(name, dev, max(5, args.steps // 5), 2))
         line["secondary"] = sec

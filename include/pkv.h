@@ -44,11 +44,13 @@
  * Call order per step (attn.dense requires_kv_write: the layer stores its K/V
  * before it runs attention):
  *   pkv_plan_create (or pkv_plan_update)    host only; never touches the device
- *   pkv_plan_upload(workspace, stream)      async H2D from library-owned pinned memory
+ *   pkv_plan_upload(workspace, stream)      async upload from library-owned pinned memory
  *   per layer: pkv_append_kv(...)           optional; stores this step's K/V
  *              pkv_run(...)                 attention for every planned query
  *          or  pkv_run_append(...)          both in one call
- * One plan serves every layer of a step.
+ * One plan serves every layer of a step.  Dense plans (PKV_KIND_DENSE) instead go
+ * pkv_dense_plan_create -> pkv_plan_upload -> per layer pkv_dense_gather,
+ * pkv_dense_run; pkv_run / pkv_append_kv / pkv_run_append reject them.
  *
  * Ownership: the caller owns every device buffer (q, out, lse, cache, workspace,
  * k_new, v_new).  The library owns the plan handle, which copies what it needs
@@ -85,8 +87,10 @@ typedef enum pkv_status {
 typedef enum pkv_kind {
   PKV_KIND_DECODE = 0,   /* one query token per row; qo_indptr is NULL (FlashInferDecodeWrapper) */
   PKV_KIND_PREFILL = 1,  /* ragged query rows (FlashInferPrefillWrapper) */
-  PKV_KIND_MIXED = 2     /* one-token rows on a decode sub-plan, other rows on a prefill
+  PKV_KIND_MIXED = 2,    /* one-token rows on a decode sub-plan, other rows on a prefill
                             sub-plan (FlashInferMixedWrapper) */
+  PKV_KIND_DENSE = 3     /* contiguous [prefix | fresh] K/V per row, cu_q / cu_k offsets
+                            (attn.dense DensePlan); built by pkv_dense_plan_create */
 } pkv_kind;
 
 typedef enum pkv_dtype { PKV_DTYPE_BF16 = 0 } pkv_dtype;
@@ -177,7 +181,8 @@ pkv_status pkv_plan_write_slots(const pkv_plan* plan, const int64_t** slots, int
  * ("moved to the front", FlashInferMixedWrapper).  n = 0 for other kinds. */
 pkv_status pkv_plan_permutation(const pkv_plan* plan, const int32_t** perm, int32_t* n);
 /* Scalars: [0] total_q, [1] batch, [2] decode rows, [3] prompt rows, [4] split-KV chunk
- * pages, [5] partial slots, [6] metadata bytes, [7] workspace bytes, [8] num_cus used. */
+ * pages, [5] partial slots, [6] metadata bytes, [7] workspace bytes, [8] num_cus used,
+ * [9] dense key rows (cu_k[batch]; 0 for paged plans). */
 pkv_status pkv_plan_info(const pkv_plan* plan, int64_t info[16]);
 
 /* Copy the plan's metadata into the head of `workspace` (device memory of at least
@@ -217,6 +222,50 @@ pkv_status pkv_append_kv(const pkv_plan* plan, const void* k_new, const void* v_
                          void* kv_cache_layer, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* ---- Dense [prefix | fresh] mode (attn.dense: DenseAttentionManager, DensePlan,
+ * DenseSegment) ----
+ * Row r's K/V are rows [cu_k[r], cu_k[r+1]) of contiguous bf16 tensors k, v
+ * [cu_k[batch], Hk, D]: the row's frozen prefix (its first cu_k[r+1] - cu_k[r] -
+ * q_len tokens) followed by its q_len = cu_q[r+1] - cu_q[r] fresh tokens, whose
+ * queries are rows [cu_q[r], cu_q[r+1]) of q.  Attention is the same as for a paged
+ * row of that length (bottom-right causal alignment, window_left).  The fresh K/V
+ * never reach the pages (requires_kv_write is False for this backend).
+ *
+ * pkv_dense_plan_create: params->kind must be PKV_KIND_DENSE; params->page_size and
+ * max_pages describe the page pool the prefixes are gathered from.  cu_q, cu_k:
+ * host int32 [batch + 1], both starting at 0 and non-decreasing, with
+ * q_len <= key count per row and each row's K below 4 GiB.  paged_kv_indptr /
+ * paged_kv_indices (both or neither, host int32): each row's pages, which must hold
+ * at least its prefix; without them pkv_dense_gather can only copy the fresh tokens.
+ * Host only; the handle is freed by pkv_plan_destroy, uploaded by pkv_plan_upload,
+ * inspected by pkv_plan_prefill_tiles / pkv_plan_info (info[9] = cu_k[batch]).
+ * Errors as pkv_plan_create. */
+pkv_status pkv_dense_plan_create(const pkv_plan_params* params, int32_t batch, const int32_t* cu_q,
+                                 const int32_t* cu_k, const int32_t* paged_kv_indptr,
+                                 const int32_t* paged_kv_indices, pkv_plan** out,
+                                 size_t* workspace_bytes);
+/* Re-plan a dense handle for a new step (same rules; the upload is invalidated). */
+pkv_status pkv_dense_plan_update(pkv_plan* plan, int32_t batch, const int32_t* cu_q,
+                                 const int32_t* cu_k, const int32_t* paged_kv_indptr,
+                                 const int32_t* paged_kv_indices, size_t* workspace_bytes);
+/* Build the contiguous K/V of an uploaded dense plan: k_out / v_out [cu_k[batch], Hk, D]
+ * receive, per row, its prefix gathered from kv_cache_layer's pages (only when
+ * with_prefix != 0) followed by its fresh tokens k_fresh / v_fresh [cu_q[batch], Hk, D]
+ * (DenseAttentionManager gathers the prefix once per stream and layer and
+ * concatenates the fresh K/V each step: call with with_prefix = 0 to refresh only the
+ * fresh rows of a buffer whose prefixes are already in place).  All device pointers
+ * 16-byte aligned.  PKV_E_INVALID if with_prefix is set on a plan without pages.
+ * Enqueued on stream; timed as kind [0]. */
+pkv_status pkv_dense_gather(const pkv_plan* plan, const void* kv_cache_layer, const void* k_fresh,
+                            const void* v_fresh, void* k_out, void* v_out, int32_t with_prefix,
+                            void* workspace, size_t workspace_bytes, void* stream);
+/* Dense attention of an uploaded dense plan: q [cu_q[batch], Hq, D], k / v
+ * [cu_k[batch], Hk, D] bf16, out like q, lse [cu_q[batch], Hq] fp32 or NULL.  Runs the
+ * prefill kernel with contiguous addressing; errors as pkv_run.  Enqueued on stream. */
+pkv_status pkv_dense_run(const pkv_plan* plan, const void* q, const void* k, const void* v,
+                         void* out, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* The page table of a step's rows without the tokens the step appends
  * (kv.plan context_only_views, for attention over the stored context alone).
  * Row r of the input table (paged_kv_indptr / _indices / _last_page_len, the same
@@ -245,7 +294,8 @@ pkv_status pkv_context_only_views(int32_t batch, int32_t page_size, const int32_
  * counterpart).  While enabled, pkv_run, pkv_run_append and pkv_append_kv record a HIP event on the
  * stream before and after every kernel they launch with this plan.
  * pkv_timing_read waits for those events, returns for each kernel kind
- * ([0] append, [1] decode, [2] split-KV merge, [3] prefill) the summed milliseconds
+ * ([0] append or dense gather, [1] decode, [2] split-KV merge, [3] prefill or dense
+ * attention) the summed milliseconds
  * and the number of launches since the last read, and clears the record.
  * Events come from a pool the plan owns (created on first use, reused after a read). */
 pkv_status pkv_timing_enable(pkv_plan* plan, int32_t enable);

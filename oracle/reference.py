@@ -18,7 +18,8 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "RowLayout", "decode_csr", "query_position", "visible_keys",
     "kv_head_of", "gather_row_kv", "attention", "attention_rows", "attention_bruteforce", "write_slots",
-    "apply_append", "mixed_permutation", "merge_partials", "context_only_views", "OracleError",
+    "apply_append", "mixed_permutation", "merge_partials", "context_only_views",
+    "attention_dense", "dense_gather", "OracleError",
 ]
 
 
@@ -215,6 +216,63 @@ def attention(q, cache, page_size, kv_indptr, kv_indices, last_page_len, *, num_
         out[qo[r]:qo[r + 1]] = o
         lse[qo[r]:qo[r + 1]] = l
     return out, lse
+
+
+def attention_dense(q, k, v, cu_q, cu_k, *, num_qo_heads, num_kv_heads, causal=True,
+                    window_left=-1):
+    """Attention over contiguous [frozen prefix | fresh tokens] K/V
+    (attn.dense, DenseAttentionManager and DensePlan): row r's queries are
+    q[cu_q[r]:cu_q[r+1]] and its keys k/v[cu_k[r]:cu_k[r+1]], the last q_len of
+    them fresh, so query t sits at position kv_len - q_len + t exactly as for a
+    paged row.  q [Tq, Hq, D], k/v [Tk, Hk, D] (bf16 bits or float64).
+    Returns (out [Tq, Hq, D], lse [Tq, Hq]) float64."""
+    cq = np.asarray(cu_q, dtype=np.int64)
+    ck = np.asarray(cu_k, dtype=np.int64)
+    Q, K, V = bf16_to_f64(q), bf16_to_f64(k), bf16_to_f64(v)
+    D = Q.shape[-1]
+    scale = 1.0 / math.sqrt(D)
+    out = np.zeros((Q.shape[0], num_qo_heads, D))
+    lse = np.zeros((Q.shape[0], num_qo_heads))
+    for r in range(len(cq) - 1):
+        L, n = int(cq[r + 1] - cq[r]), int(ck[r + 1] - ck[r])
+        if L > n:
+            raise OracleError(f"row {r}: q_len {L} > kv_len {n}")
+        if L == 0:
+            continue
+        pos = np.array([query_position(n, L, t) for t in range(L)], dtype=np.int64)
+        for h in range(num_qo_heads):
+            hk = kv_head_of(h, num_qo_heads, num_kv_heads)
+            o, l = _attend_head(Q[cq[r]:cq[r + 1], h], K[ck[r]:ck[r + 1], hk],
+                                V[ck[r]:ck[r + 1], hk], pos, n, causal, window_left, scale)
+            out[cq[r]:cq[r + 1], h], lse[cq[r]:cq[r + 1], h] = o, l
+    return out, lse
+
+
+def dense_gather(cache_bits, page_size, kv_indptr, kv_indices, cu_q, cu_k, k_fresh_bits,
+                 v_fresh_bits, *, with_prefix=True, k_out=None, v_out=None):
+    """Contiguous K/V of a dense plan (DenseAttentionManager: the prefix is
+    gathered from the pages, the step's fresh K/V concatenated after it).
+    Row r's prefix is its first (cu_k[r+1]-cu_k[r]) - (cu_q[r+1]-cu_q[r]) tokens,
+    token j on page kv_indices[kv_indptr[r] + j // page_size] at slot
+    j % page_size; its fresh tokens are k/v_fresh[cu_q[r]:cu_q[r+1]].  Bit
+    copies (uint16).  with_prefix=False leaves the prefix rows of k_out/v_out as
+    given.  Returns (k_out, v_out) [cu_k[-1], Hk, D]."""
+    cq = np.asarray(cu_q, dtype=np.int64)
+    ck = np.asarray(cu_k, dtype=np.int64)
+    shape = (int(ck[-1]),) + tuple(k_fresh_bits.shape[1:])
+    ko = np.zeros(shape, np.uint16) if k_out is None else k_out.copy()
+    vo = np.zeros(shape, np.uint16) if v_out is None else v_out.copy()
+    for r in range(len(cq) - 1):
+        L, n = int(cq[r + 1] - cq[r]), int(ck[r + 1] - ck[r])
+        P = n - L
+        if with_prefix:
+            for j in range(P):
+                page = int(kv_indices[int(kv_indptr[r]) + j // page_size])
+                ko[ck[r] + j] = cache_bits[page, 0, j % page_size]
+                vo[ck[r] + j] = cache_bits[page, 1, j % page_size]
+        ko[ck[r] + P:ck[r + 1]] = k_fresh_bits[cq[r]:cq[r + 1]]
+        vo[ck[r] + P:ck[r + 1]] = v_fresh_bits[cq[r]:cq[r + 1]]
+    return ko, vo
 
 
 def attention_bruteforce(q, cache, page_size, kv_indptr, kv_indices, last_page_len, *,

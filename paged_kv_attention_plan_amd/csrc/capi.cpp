@@ -156,6 +156,8 @@ pkv_status pkv_plan_create(const pkv_plan_params* params, int32_t batch, const i
   std::string err;
   pkv_status st = pkv::check_params(*params, err);
   if (st != PKV_OK) return fail(st, err);
+  if (params->kind == PKV_KIND_DENSE)
+    return fail(PKV_E_INVALID, "dense plans are built by pkv_dense_plan_create");
   int32_t cus = 0;
   st = resolve_cus(params, &cus);
   if (st != PKV_OK) return st;
@@ -179,6 +181,7 @@ pkv_status pkv_plan_update(pkv_plan* plan, int32_t batch, const int32_t* qo_indp
   g_err.clear();
   if (plan == nullptr || workspace_bytes == nullptr)
     return fail(PKV_E_INVALID, "plan and workspace_bytes must not be NULL");
+  if (plan->d.dense) return fail(PKV_E_INVALID, "dense plans are re-planned by pkv_dense_plan_update");
   pkv::PlanData fresh;
   std::string err;
   pkv_status st = pkv::build_plan(plan->d.params, plan->d.num_cus, batch, qo_indptr,
@@ -249,6 +252,13 @@ pkv_status pkv_plan_info(const pkv_plan* plan, int64_t info[16]) {
   info[6] = (int64_t)d.ws.meta_bytes;
   info[7] = (int64_t)d.ws.total_bytes;
   info[8] = d.num_cus;
+  info[9] = d.total_k;
+  return PKV_OK;
+}
+
+static pkv_status check_paged(const pkv_plan* plan) {
+  if (plan != nullptr && plan->d.dense)
+    return fail(PKV_E_INVALID, "a dense plan runs through pkv_dense_gather / pkv_dense_run");
   return PKV_OK;
 }
 
@@ -312,6 +322,7 @@ namespace {
 pkv_status check_run(const pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
                      float* lse, void* workspace, size_t workspace_bytes) {
   if (plan == nullptr) return fail(PKV_E_INVALID, "plan must not be NULL");
+  if (check_paged(plan) != PKV_OK) return PKV_E_INVALID;
   pkv_status st = check_workspace(plan, workspace, workspace_bytes);
   if (st != PKV_OK) return st;
   if (plan->uploaded_ws != workspace)
@@ -430,6 +441,7 @@ pkv_status pkv_append_kv(const pkv_plan* plan, const void* k_new, const void* v_
                          void* stream) {
   g_err.clear();
   if (plan == nullptr) return fail(PKV_E_INVALID, "plan must not be NULL");
+  if (check_paged(plan) != PKV_OK) return PKV_E_INVALID;
   pkv_status st = check_workspace(plan, workspace, workspace_bytes);
   if (st != PKV_OK) return st;
   if (plan->uploaded_ws != workspace)
@@ -453,6 +465,142 @@ pkv_status pkv_append_kv(const pkv_plan* plan, const void* k_new, const void* v_
   PKV_HIP(timing_mark(plan, s, kAppend, true));
   PKV_HIP(pkv::launch_append(a, s));
   PKV_HIP(timing_mark(plan, s, kAppend, false));
+  return PKV_OK;
+}
+
+pkv_status pkv_dense_plan_create(const pkv_plan_params* params, int32_t batch, const int32_t* cu_q,
+                                 const int32_t* cu_k, const int32_t* paged_kv_indptr,
+                                 const int32_t* paged_kv_indices, pkv_plan** out,
+                                 size_t* workspace_bytes) {
+  g_err.clear();
+  if (params == nullptr || out == nullptr || workspace_bytes == nullptr)
+    return fail(PKV_E_INVALID, "params, out and workspace_bytes must not be NULL");
+  *out = nullptr;
+  std::string err;
+  pkv_status st = pkv::check_params(*params, err);
+  if (st != PKV_OK) return fail(st, err);
+  int32_t cus = 0;
+  st = resolve_cus(params, &cus);
+  if (st != PKV_OK) return st;
+  pkv_plan* p = new (std::nothrow) pkv_plan;
+  if (p == nullptr) return fail(PKV_E_INVALID, "out of host memory");
+  st = pkv::build_dense_plan(*params, cus, batch, cu_q, cu_k, paged_kv_indptr, paged_kv_indices,
+                             p->d, err);
+  if (st != PKV_OK) {
+    delete p;
+    return fail(st, err);
+  }
+  *workspace_bytes = p->d.ws.total_bytes;
+  *out = p;
+  return PKV_OK;
+}
+
+pkv_status pkv_dense_plan_update(pkv_plan* plan, int32_t batch, const int32_t* cu_q,
+                                 const int32_t* cu_k, const int32_t* paged_kv_indptr,
+                                 const int32_t* paged_kv_indices, size_t* workspace_bytes) {
+  g_err.clear();
+  if (plan == nullptr || workspace_bytes == nullptr)
+    return fail(PKV_E_INVALID, "plan and workspace_bytes must not be NULL");
+  if (!plan->d.dense) return fail(PKV_E_INVALID, "not a dense plan (use pkv_plan_update)");
+  pkv::PlanData fresh;
+  std::string err;
+  pkv_status st = pkv::build_dense_plan(plan->d.params, plan->d.num_cus, batch, cu_q, cu_k,
+                                        paged_kv_indptr, paged_kv_indices, fresh, err);
+  if (st != PKV_OK) return fail(st, err);
+  plan->d = std::move(fresh);
+  plan->uploaded_ws = nullptr;
+  *workspace_bytes = plan->d.ws.total_bytes;
+  return PKV_OK;
+}
+
+static pkv_status check_dense(const pkv_plan* plan, void* workspace, size_t workspace_bytes) {
+  if (plan == nullptr) return fail(PKV_E_INVALID, "plan must not be NULL");
+  if (!plan->d.dense) return fail(PKV_E_INVALID, "not a dense plan (use pkv_run)");
+  pkv_status st = check_workspace(plan, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  if (plan->uploaded_ws != workspace)
+    return fail(PKV_E_STATE, "the plan was not uploaded to this workspace (call pkv_plan_upload first)");
+  return PKV_OK;
+}
+
+pkv_status pkv_dense_gather(const pkv_plan* plan, const void* kv_cache_layer, const void* k_fresh,
+                            const void* v_fresh, void* k_out, void* v_out, int32_t with_prefix,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  pkv_status st = check_dense(plan, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  const pkv::PlanData& d = plan->d;
+  if (d.total_k == 0) return PKV_OK;
+  if (k_out == nullptr || v_out == nullptr || !aligned16(k_out) || !aligned16(v_out))
+    return fail(PKV_E_INVALID, "k_out and v_out must be non-NULL and 16-byte aligned");
+  if (d.total_q > 0 && (k_fresh == nullptr || v_fresh == nullptr || !aligned16(k_fresh) ||
+                        !aligned16(v_fresh)))
+    return fail(PKV_E_INVALID, "k_fresh and v_fresh must be non-NULL and 16-byte aligned");
+  if (with_prefix) {
+    if (!d.dense_pages)
+      return fail(PKV_E_INVALID, "the plan has no page table: gather with with_prefix = 0");
+    if (kv_cache_layer == nullptr || !aligned16(kv_cache_layer))
+      return fail(PKV_E_INVALID, "kv_cache_layer must be non-NULL and 16-byte aligned");
+  }
+  char* ws = static_cast<char*>(workspace);
+  pkv::GatherArgs a{};
+  a.rows = reinterpret_cast<const pkv::DenseRowMeta*>(ws + d.ws.off_dense_rows);
+  a.n_rows = d.batch;
+  a.with_prefix = with_prefix ? 1 : 0;
+  a.total_k = d.total_k;
+  a.total_q = d.total_q;
+  a.indices = reinterpret_cast<const int32_t*>(ws + d.ws.off_indices);
+  a.cache = static_cast<const uint16_t*>(kv_cache_layer);
+  a.k_fresh = static_cast<const uint16_t*>(k_fresh);
+  a.v_fresh = static_cast<const uint16_t*>(v_fresh);
+  a.k_out = static_cast<uint16_t*>(k_out);
+  a.v_out = static_cast<uint16_t*>(v_out);
+  a.num_kv_heads = d.params.num_kv_heads;
+  a.head_dim = d.params.head_dim;
+  a.page_size = d.params.page_size;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PKV_HIP(timing_mark(plan, s, kAppend, true));
+  PKV_HIP(pkv::launch_gather(a, s));
+  PKV_HIP(timing_mark(plan, s, kAppend, false));
+  return PKV_OK;
+}
+
+pkv_status pkv_dense_run(const pkv_plan* plan, const void* q, const void* k, const void* v,
+                         void* out, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  g_err.clear();
+  pkv_status st = check_dense(plan, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  const pkv::PlanData& d = plan->d;
+  if (d.prefill_tiles.empty()) return PKV_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(PKV_E_INVALID, "q, k, v and out must not be NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
+    return fail(PKV_E_INVALID, "q, k, v, out and workspace must be 16-byte aligned");
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return fail(PKV_E_INVALID, "lse must be 4-byte aligned");
+  const pkv_plan_params& P = d.params;
+  char* ws = static_cast<char*>(workspace);
+  pkv::PrefillArgs a{};
+  a.tiles = reinterpret_cast<const pkv_prefill_tile*>(ws + d.ws.off_prefill_tiles);
+  a.n_tiles = (int32_t)d.prefill_tiles.size();
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_dense = static_cast<const uint16_t*>(k);
+  a.v_dense = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.num_qo_heads = P.num_qo_heads;
+  a.num_kv_heads = P.num_kv_heads;
+  a.head_dim = P.head_dim;
+  a.page_size = P.page_size;
+  a.group = d.group;
+  a.causal = P.causal ? 1 : 0;
+  a.window_left = P.window_left;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.head_dim));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PKV_HIP(timing_mark(plan, s, kPrefill, true));
+  PKV_HIP(pkv::launch_prefill(a, s));
+  PKV_HIP(timing_mark(plan, s, kPrefill, false));
   return PKV_OK;
 }
 

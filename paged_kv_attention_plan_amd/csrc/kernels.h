@@ -51,12 +51,34 @@ struct PrefillArgs {
   const int32_t* indices;
   const uint16_t* q;
   const uint16_t* cache;
+  // Dense mode (both non-null): contiguous K and V, bf16 [total_k, Hk, D]; a
+  // tile's keys start at row page_base (cu_k of its row); cache and indices
+  // are unused.
+  const uint16_t* k_dense;
+  const uint16_t* v_dense;
   uint16_t* out;
   float* lse;
   int32_t num_qo_heads, num_kv_heads, head_dim, page_size, group;
   int32_t causal, window_left;
   float scale_log2;
 };
+
+struct GatherArgs {
+  const DenseRowMeta* rows;
+  int32_t n_rows;
+  int32_t with_prefix;      // 0: copy the fresh tokens only
+  int64_t total_k;          // dense rows = cu_k of the end
+  int32_t total_q;          // fresh tokens = cu_q of the end
+  const int32_t* indices;
+  const uint16_t* cache;    // bf16 [max_pages, 2, ps, Hk, D]
+  const uint16_t* k_fresh;  // bf16 [total_q, Hk, D]
+  const uint16_t* v_fresh;
+  uint16_t* k_out;          // bf16 [total_k, Hk, D]
+  uint16_t* v_out;
+  int32_t num_kv_heads, head_dim, page_size;
+};
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 
 // Plan metadata upload: the GPU copies n_vec 16-byte vectors from page-locked
 // host memory (device-visible pointer) into the workspace.  Workgroup b then

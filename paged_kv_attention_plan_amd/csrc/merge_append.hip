@@ -1,4 +1,4 @@
-// Split-KV merge, KV append and the plan metadata upload.
+// Split-KV merge, KV append, the plan metadata upload and the dense gather.
 //
 // Merge (the workspace page, mstar attn.workspace, keeps split-KV partials):
 // a row whose keys were cut into chunks c has, per query head, a partial output
@@ -158,6 +158,48 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   for (int i = i0 + blockDim.x; i < 2 * nvec; i += blockDim.x) store(i, i < nvec ? sk[i] : sv[i - nvec]);
 }
 
+// Dense gather (attn.dense DenseAttentionManager: the frozen prefix gathered
+// from the pages and the step's fresh K/V concatenated after it): one wave per
+// copied token.  With the prefix, wave t copies dense row t, and its (request)
+// row is the last with cu_k <= t; without it, wave t copies fresh token t, and
+// its row is the last with cu_q <= t.  Rows are found by binary search over
+// the row table.
+__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= (a.with_prefix ? a.total_k : (int64_t)a.total_q)) return;
+  int lo = 0, hi = a.n_rows - 1;  // rows[0] starts at 0, so rows[lo] starts at or before t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((a.with_prefix ? a.rows[mid].cu_k : a.rows[mid].cu_q) <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  const DenseRowMeta rm = a.rows[lo];
+  // key index within the row and the dense row it goes to
+  const int j = a.with_prefix ? (int)(t - rm.cu_k) : rm.prefix + (int)(t - rm.cu_q);
+  const int64_t dst_row = (int64_t)rm.cu_k + j;
+  const int row = a.num_kv_heads * a.head_dim;
+  const int nvec = row / 8;
+  const uint16_t* src_k;
+  const uint16_t* src_v;
+  if (j < rm.prefix) {
+    const int ps = a.page_size;
+    const int64_t page = a.indices[rm.page_base + (j >> __builtin_ctz(ps))];
+    src_k = a.cache + ((page * 2 + 0) * ps + (j & (ps - 1))) * (int64_t)row;
+    src_v = src_k + (int64_t)ps * row;
+  } else {
+    const int64_t f = (int64_t)rm.cu_q + (j - rm.prefix);
+    src_k = a.k_fresh + f * row;
+    src_v = a.v_fresh + f * row;
+  }
+  uint4* dk = reinterpret_cast<uint4*>(a.k_out + dst_row * row);
+  uint4* dv = reinterpret_cast<uint4*>(a.v_out + dst_row * row);
+  for (int i = lane; i < 2 * nvec; i += 64) {
+    if (i < nvec) dk[i] = reinterpret_cast<const uint4*>(src_k)[i];
+    else dv[i - nvec] = reinterpret_cast<const uint4*>(src_v)[i - nvec];
+  }
+}
+
 __global__ __launch_bounds__(256) void upload_kernel(UploadArgs a) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.n_vec; i += stride)
@@ -180,6 +222,15 @@ hipError_t launch_upload(const UploadArgs& a, hipStream_t stream, int* blocks) {
   nb = nb > a.max_blocks ? a.max_blocks : nb;
   hipLaunchKernelGGL(upload_kernel, dim3((unsigned)nb), dim3(256), 0, stream, a);
   *blocks = (int)nb;
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
+  const int64_t n = a.with_prefix ? a.total_k : (int64_t)a.total_q;  // waves
+  if (n <= 0 || a.n_rows <= 0) return hipSuccess;
+  const int64_t blocks = (n + 3) / 4;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-// Device-side form of a decode plan, as uploaded to the workspace.  The public
+// Device-side form of a plan's rows and tiles, as uploaded to the workspace.  The public
 // structs of pkv.h (pkv_decode_tile, pkv_merge_entry) stay the inspection view;
 // this form is what the decode kernel reads: a 16-byte tile plus a per-row
 // table, so the per-step upload is about half the size.
@@ -27,6 +27,16 @@ struct DecodeTileMeta {
   int32_t kv_end;
 };
 
+// One row of a dense plan, for the gather: the row's keys are dense rows
+// [cu_k, cu_k + prefix + fresh); the prefix comes from the pages
+// indices[page_base ..], the fresh part from rows [cu_q, cu_q + fresh) of the
+// step's K/V.
+struct DenseRowMeta {
+  int32_t cu_k, cu_q, prefix, fresh, page_base;
+  int32_t pad[3];
+};
+
+static_assert(sizeof(DenseRowMeta) == 32, "dense rows are 32 bytes");
 static_assert(sizeof(DecodeRowMeta) == 32, "row table entries are 32 bytes");
 static_assert(sizeof(DecodeTileMeta) == 16, "decode tiles are 16 bytes");
 

@@ -38,11 +38,60 @@ std::string fmt_row(const char* what, int64_t r) {
   return std::string(what) + " (row " + std::to_string(r) + ")";
 }
 
+// Prefill tiles of the given rows (FlashInferPrefillWrapper.plan): blocks of
+// 128 / group query tokens per KV head, keys [lo(first token), hi(last token)],
+// sorted by key count descending, ties by (row, block, head).  page_base(r) is
+// where row r's keys start: its first page-table entry, or its first dense row.
+template <class PageBase>
+void make_prefill_tiles(const pkv_plan_params& P, const std::vector<int32_t>& rows,
+                        const std::vector<int32_t>& kv_len, const std::vector<int32_t>& q_len,
+                        const std::vector<int32_t>& q_start, PageBase page_base,
+                        std::vector<pkv_prefill_tile>& tiles) {
+  if (rows.empty()) return;
+  const int32_t Hk = P.num_kv_heads;
+  const int64_t bt = 128 / (P.num_qo_heads / Hk);
+  const int64_t w = P.window_left;
+  struct Item { int64_t keys; int32_t r, b, hk; pkv_prefill_tile t; };
+  std::vector<Item> items;
+  for (int32_t r : rows) {
+    const int64_t n = kv_len[r], L = q_len[r];
+    for (int64_t b = 0; b * bt < L; ++b) {
+      const int64_t qs = b * bt, qc = std::min(bt, L - qs);
+      const int64_t p0 = n - L + qs, p1 = p0 + qc - 1;
+      const int64_t lo = w < 0 ? 0 : std::max<int64_t>(0, p0 - w);
+      const int64_t hi = P.causal ? p1 : n - 1;
+      for (int32_t hk = 0; hk < Hk; ++hk) {
+        pkv_prefill_tile t{};
+        t.row = r;
+        t.kv_head = hk;
+        t.q_start = (int32_t)qs;
+        t.q_count = (int32_t)qc;
+        t.kv_lo = (int32_t)lo;
+        t.kv_hi = (int32_t)hi;
+        t.page_base = page_base(r);
+        t.q_base = q_start[r];
+        t.kv_len = (int32_t)n;
+        t.q_len = (int32_t)L;
+        items.push_back({hi - lo + 1, r, (int32_t)b, hk, t});
+      }
+    }
+  }
+  std::sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
+    if (a.keys != b.keys) return a.keys > b.keys;
+    if (a.r != b.r) return a.r < b.r;
+    if (a.b != b.b) return a.b < b.b;
+    return a.hk < b.hk;
+  });
+  tiles.reserve(items.size());
+  for (auto& it : items) tiles.push_back(it.t);
+}
+
+
 }  // namespace
 
 pkv_status check_params(const pkv_plan_params& p, std::string& err) {
-  if (p.kind < PKV_KIND_DECODE || p.kind > PKV_KIND_MIXED) {
-    err = "kind must be PKV_KIND_DECODE, PKV_KIND_PREFILL or PKV_KIND_MIXED";
+  if (p.kind < PKV_KIND_DECODE || p.kind > PKV_KIND_DENSE) {
+    err = "kind must be PKV_KIND_DECODE, PKV_KIND_PREFILL, PKV_KIND_MIXED or PKV_KIND_DENSE";
     return PKV_E_INVALID;
   }
   if (p.num_qo_heads < 1 || p.num_kv_heads < 1 || p.num_qo_heads % p.num_kv_heads != 0) {
@@ -71,7 +120,8 @@ pkv_status check_params(const pkv_plan_params& p, std::string& err) {
     return PKV_E_INVALID;
   }
   const int g = p.num_qo_heads / p.num_kv_heads;
-  if (p.kind != PKV_KIND_PREFILL && !(g == 1 || g == 2 || g == 4 || g == 8)) {
+  if ((p.kind == PKV_KIND_DECODE || p.kind == PKV_KIND_MIXED) &&
+      !(g == 1 || g == 2 || g == 4 || g == 8)) {
     err = "decode rows need num_qo_heads / num_kv_heads in {1, 2, 4, 8} (got " + std::to_string(g) + ")";
     return PKV_E_UNSUPPORTED;
   }
@@ -88,6 +138,35 @@ pkv_status check_params(const pkv_plan_params& p, std::string& err) {
     return PKV_E_INVALID;
   }
   return PKV_OK;
+}
+
+// Byte offsets of the workspace regions (256-byte aligned): metadata first,
+// then the split-KV partials.
+void layout_workspace(PlanData& plan) {
+  const pkv_plan_params& P = plan.params;
+  const int32_t g = plan.group;
+  WorkspaceLayout& L = plan.ws;
+  size_t off = kAlign;  // first 256 bytes reserved
+  L.off_dense_rows = off;
+  off = align_up(off + plan.dense_rows.size() * sizeof(DenseRowMeta));
+  L.off_decode_rows = off;
+  off = align_up(off + plan.decode_rows.size() * sizeof(DecodeRowMeta));
+  L.off_decode_tiles = off;
+  off = align_up(off + plan.decode_tile_meta.size() * sizeof(DecodeTileMeta));
+  L.off_merges = off;
+  off = align_up(off + plan.merges.size() * sizeof(pkv_merge_entry));
+  L.off_prefill_tiles = off;
+  off = align_up(off + plan.prefill_tiles.size() * sizeof(pkv_prefill_tile));
+  L.off_indices = off;
+  off = align_up(off + plan.indices.size() * sizeof(int32_t));
+  L.off_slots = off;
+  off = align_up(off + plan.slots.size() * sizeof(int64_t));
+  L.meta_bytes = off;
+  L.off_part_o = off;
+  off = align_up(off + (size_t)plan.n_slots * g * P.head_dim * sizeof(float));
+  L.off_part_lse = off;
+  off = align_up(off + (size_t)plan.n_slots * g * sizeof(float));
+  L.total_bytes = off;
 }
 
 pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
@@ -308,65 +387,10 @@ pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
   plan.n_slots = (int32_t)slot;
 
   // ---- prefill tiles ----
-  if (!pre_rows.empty()) {
-    const int64_t bt = 128 / g;
-    struct Item { int64_t keys; int32_t r, b, hk; pkv_prefill_tile t; };
-    std::vector<Item> items;
-    for (int32_t r : pre_rows) {
-      const int64_t n = kv_len[r], L = q_len[r];
-      for (int64_t b = 0; b * bt < L; ++b) {
-        const int64_t qs = b * bt, qc = std::min(bt, L - qs);
-        const int64_t p0 = n - L + qs, p1 = p0 + qc - 1;
-        const int64_t lo = w < 0 ? 0 : std::max<int64_t>(0, p0 - w);
-        const int64_t hi = P.causal ? p1 : n - 1;
-        for (int32_t hk = 0; hk < Hk; ++hk) {
-          pkv_prefill_tile t{};
-          t.row = r;
-          t.kv_head = hk;
-          t.q_start = (int32_t)qs;
-          t.q_count = (int32_t)qc;
-          t.kv_lo = (int32_t)lo;
-          t.kv_hi = (int32_t)hi;
-          t.page_base = kv_indptr[r];
-          t.q_base = q_start[r];
-          t.kv_len = (int32_t)n;
-          t.q_len = (int32_t)L;
-          items.push_back({hi - lo + 1, r, (int32_t)b, hk, t});
-        }
-      }
-    }
-    std::sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
-      if (a.keys != b.keys) return a.keys > b.keys;
-      if (a.r != b.r) return a.r < b.r;
-      if (a.b != b.b) return a.b < b.b;
-      return a.hk < b.hk;
-    });
-    plan.prefill_tiles.reserve(items.size());
-    for (auto& it : items) plan.prefill_tiles.push_back(it.t);
-  }
+  make_prefill_tiles(P, pre_rows, kv_len, q_len, q_start,
+                     [&](int32_t r) { return kv_indptr[r]; }, plan.prefill_tiles);
 
-  // ---- workspace layout ----
-  WorkspaceLayout& L = plan.ws;
-  size_t off = kAlign;  // first 256 bytes reserved
-  L.off_decode_rows = off;
-  off = align_up(off + plan.decode_rows.size() * sizeof(DecodeRowMeta));
-  L.off_decode_tiles = off;
-  off = align_up(off + plan.decode_tile_meta.size() * sizeof(DecodeTileMeta));
-  L.off_merges = off;
-  off = align_up(off + plan.merges.size() * sizeof(pkv_merge_entry));
-  L.off_prefill_tiles = off;
-  off = align_up(off + plan.prefill_tiles.size() * sizeof(pkv_prefill_tile));
-  L.off_indices = off;
-  off = align_up(off + plan.indices.size() * sizeof(int32_t));
-  L.off_slots = off;
-  off = align_up(off + plan.slots.size() * sizeof(int64_t));
-  L.meta_bytes = off;
-  L.off_part_o = off;
-  off = align_up(off + (size_t)plan.n_slots * g * P.head_dim * sizeof(float));
-  L.off_part_lse = off;
-  off = align_up(off + (size_t)plan.n_slots * g * sizeof(float));
-  L.total_bytes = off;
-
+  layout_workspace(plan);
   out = std::move(plan);
   return PKV_OK;
 }
@@ -381,6 +405,8 @@ void serialize_meta(const PlanData& plan, void* dst) {
   auto put = [&](size_t off, const void* src, size_t bytes) {
     if (bytes) std::memcpy(base + off, src, bytes);
   };
+  put(plan.ws.off_dense_rows, plan.dense_rows.data(),
+      plan.dense_rows.size() * sizeof(DenseRowMeta));
   put(plan.ws.off_decode_rows, plan.decode_rows.data(),
       plan.decode_rows.size() * sizeof(DecodeRowMeta));
   put(plan.ws.off_decode_tiles, plan.decode_tile_meta.data(),
@@ -456,6 +482,101 @@ pkv_status context_only_views(int32_t batch, int32_t page_size, const int32_t* k
     out_last_page_len[r] = (int32_t)(kept - (kp - 1) * page_size);
     out_qo_indptr[r + 1] = (int32_t)nq;
   }
+  return PKV_OK;
+}
+
+// attn.dense DensePlan: row r's queries are rows [cu_q[r], cu_q[r+1]) of q and
+// its keys rows [cu_k[r], cu_k[r+1]) of the contiguous K/V, the last q_len of
+// them fresh (bottom-right causal alignment as for a paged row).
+pkv_status build_dense_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
+                            const int32_t* cu_q, const int32_t* cu_k, const int32_t* kv_indptr,
+                            const int32_t* kv_indices, PlanData& out, std::string& err) {
+  pkv_status st = check_params(P, err);
+  if (st != PKV_OK) return st;
+  if (P.kind != PKV_KIND_DENSE) {
+    err = "a dense plan needs kind PKV_KIND_DENSE";
+    return PKV_E_INVALID;
+  }
+  if (num_cus < 1 || batch < 0) {
+    err = "num_cus must be >= 1 and batch >= 0";
+    return PKV_E_INVALID;
+  }
+  if (cu_q == nullptr || cu_k == nullptr) {
+    err = "cu_q and cu_k are required";
+    return PKV_E_INVALID;
+  }
+  if ((kv_indptr == nullptr) != (kv_indices == nullptr)) {
+    err = "paged_kv_indptr and paged_kv_indices must both be given or both be NULL";
+    return PKV_E_INVALID;
+  }
+  if (cu_q[0] != 0 || cu_k[0] != 0) {
+    err = "cu_q[0] and cu_k[0] must be 0";
+    return PKV_E_INVALID;
+  }
+  const bool pages = kv_indptr != nullptr;
+  if (pages && kv_indptr[0] != 0) {
+    err = "paged_kv_indptr[0] must be 0";
+    return PKV_E_INVALID;
+  }
+  const int64_t ps = P.page_size;
+  const int64_t row_bytes = (int64_t)P.num_kv_heads * P.head_dim * 2;
+  PlanData plan;
+  plan.params = P;
+  plan.batch = batch;
+  plan.num_cus = num_cus;
+  plan.group = P.num_qo_heads / P.num_kv_heads;
+  plan.dense = true;
+  plan.dense_pages = pages;
+  std::vector<int32_t> kv_len(batch), q_len(batch), q_start(batch), rows;
+  for (int32_t r = 0; r < batch; ++r) {
+    const int64_t L = (int64_t)cu_q[r + 1] - cu_q[r], N = (int64_t)cu_k[r + 1] - cu_k[r];
+    if (L < 0 || N < 0) {
+      err = fmt_row("cu_q and cu_k must be non-decreasing", r);
+      return PKV_E_INVALID;
+    }
+    if (L > N) {
+      err = fmt_row("a row's query count must not exceed its key count", r);
+      return PKV_E_INVALID;
+    }
+    // the kernel addresses a row's keys with 32-bit byte offsets
+    if ((N + 64) * row_bytes >= (int64_t)1 << 32) {
+      err = fmt_row("a row's K (or V) must stay below 4 GiB", r);
+      return PKV_E_INVALID;
+    }
+    const int64_t prefix = N - L;
+    DenseRowMeta m{};
+    m.cu_k = cu_k[r];
+    m.cu_q = cu_q[r];
+    m.prefix = (int32_t)prefix;
+    m.fresh = (int32_t)L;
+    if (pages) {
+      const int64_t np = (int64_t)kv_indptr[r + 1] - kv_indptr[r];
+      if (np < 0 || np * ps < prefix) {
+        err = fmt_row("the row's pages hold fewer tokens than its prefix", r);
+        return PKV_E_INVALID;
+      }
+      for (int64_t i = 0; i < (prefix + ps - 1) / ps; ++i) {
+        const int32_t id = kv_indices[kv_indptr[r] + i];
+        if (id < 0 || id >= P.max_pages) {
+          err = fmt_row("page id outside [0, max_pages)", r);
+          return PKV_E_INVALID;
+        }
+      }
+      m.page_base = kv_indptr[r];
+    }
+    plan.dense_rows.push_back(m);
+    kv_len[r] = (int32_t)N;
+    q_len[r] = (int32_t)L;
+    q_start[r] = cu_q[r];
+    if (L >= 1) rows.push_back(r);
+  }
+  plan.total_q = batch > 0 ? cu_q[batch] : 0;
+  plan.total_k = batch > 0 ? cu_k[batch] : 0;
+  if (pages) plan.indices.assign(kv_indices, kv_indices + (batch > 0 ? kv_indptr[batch] : 0));
+  make_prefill_tiles(P, rows, kv_len, q_len, q_start, [&](int32_t r) { return cu_k[r]; },
+                     plan.prefill_tiles);
+  layout_workspace(plan);
+  out = std::move(plan);
   return PKV_OK;
 }
 

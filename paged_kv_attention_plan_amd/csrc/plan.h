@@ -17,6 +17,7 @@ namespace pkv {
 // regions [0, meta_bytes) are filled by the upload; the partial regions are
 // scratch written by split decode tiles and read by the merge.
 struct WorkspaceLayout {
+  size_t off_dense_rows = 0;      // DenseRowMeta per row of a dense plan
   size_t off_decode_rows = 0;     // DecodeRowMeta per decode row
   size_t off_decode_tiles = 0;    // DecodeTileMeta per decode tile
   size_t off_merges = 0;          // pkv_merge_entry per split (row, KV head)
@@ -48,6 +49,11 @@ struct PlanData {
   std::vector<int32_t> indices;  // copy of paged_kv_indices
   std::vector<int64_t> slots;    // flat write slot per query token
   std::vector<int32_t> perm;     // mixed: prompt tokens first
+  // dense plans
+  bool dense = false;
+  bool dense_pages = false;      // page table given: the gather may copy prefixes
+  int64_t total_k = 0;           // cu_k[batch]
+  std::vector<DenseRowMeta> dense_rows;
   WorkspaceLayout ws;
 };
 
@@ -57,6 +63,13 @@ pkv_status build_plan(const pkv_plan_params& params, int32_t num_cus, int32_t ba
                       const int32_t* qo_indptr, const int32_t* kv_indptr,
                       const int32_t* kv_indices, const int32_t* last_page_len,
                       const int32_t* kv_lens, PlanData& out, std::string& err);
+
+// Dense plan (kind PKV_KIND_DENSE): rows of contiguous K/V at cu_k offsets with
+// queries at cu_q offsets; kv_indptr / kv_indices (both or neither) give each
+// row's pages for gathering its prefix (the first cu_k - cu_q tokens).
+pkv_status build_dense_plan(const pkv_plan_params& params, int32_t num_cus, int32_t batch,
+                            const int32_t* cu_q, const int32_t* cu_k, const int32_t* kv_indptr,
+                            const int32_t* kv_indices, PlanData& out, std::string& err);
 
 // Parameter checks that do not need the page table.
 pkv_status check_params(const pkv_plan_params& p, std::string& err);

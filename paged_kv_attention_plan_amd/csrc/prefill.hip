@@ -72,7 +72,9 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
 
 // WAVE_PAGE: page_size >= 16, so the 16 keys a wave stages per tile lie in one
 // page -- its id is a scalar load and the loads use a scalar base.
-template <int D, bool WAVE_PAGE>
+// DENSE (with WAVE_PAGE): the keys are contiguous rows of k_dense / v_dense
+// starting at the tile's page_base; the row acts as one page.
+template <int D, bool WAVE_PAGE, bool DENSE>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   constexpr int BN = 64;              // keys per tile
   constexpr int KSTEPS = D / 16;      // MFMA steps over head_dim for S
@@ -173,7 +175,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     return kstart + t * BN + 16 * wave;
   };
   auto load_pids = [&](int t, int (&pid)[KPT]) {
-    if constexpr (WAVE_PAGE) {
+    if constexpr (DENSE) {
+      pid[0] = 0;  // no page table
+    } else if constexpr (WAVE_PAGE) {
       const int k0 = wave_key0(t);
       const int k0c = k0 < kv_len ? k0 : kv_len - 1;
       pid[0] = cidx[page_base + (k0c >> ps_log2)];  // uniform: scalar load
@@ -192,7 +196,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   u32x4_t gk[KPT], gv[KPT];
   // Global loads of tile t into registers: K (kv = 0) into gk, V (kv = 1) into gv.
   auto gload = [&](int t, const int (&pid)[KPT], int kv, u32x4_t (&dst)[KPT]) {
-    if constexpr (WAVE_PAGE) {
+    if constexpr (DENSE) {
+      // key k0 + tk + i of the row at byte (k0 + tk + i) * row_bytes, clamped to
+      // the row's last key
+      const char* base_p = reinterpret_cast<const char*>(kv ? a.v_dense : a.k_dense) +
+                           (int64_t)page_base * row_bytes + head_bytes;
+      const int k0 = wave_key0(t);
+      const uint32_t base = (uint32_t)k0 * row_bytes;
+      const uint32_t lim = (uint32_t)(kv_len - 1) * row_bytes + seg * 16u;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i)
+        dst[i] = *reinterpret_cast<const u32x4_t*>(base_p + min(base + toff[i], lim));
+    } else if constexpr (WAVE_PAGE) {
       const char* base_p = reinterpret_cast<const char*>(a.cache) +
                            (int64_t)pid[0] * page_elems * 2 + head_bytes +
                            (kv ? (int64_t)v_off * 2 : 0);
@@ -428,10 +443,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 template <int D>
 hipError_t launch_d(const PrefillArgs& a, hipStream_t stream) {
   const dim3 grid(a.n_tiles), block(256);
-  if (a.page_size >= 16)
-    hipLaunchKernelGGL((prefill_kernel<D, true>), grid, block, 0, stream, a);
+  if (a.k_dense != nullptr)
+    hipLaunchKernelGGL((prefill_kernel<D, true, true>), grid, block, 0, stream, a);
+  else if (a.page_size >= 16)
+    hipLaunchKernelGGL((prefill_kernel<D, true, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -18,9 +18,9 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 # ---- status codes and enums (pkv.h) ----
 OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_CAPACITY, E_CONFLICT, E_DEVICE, E_STATE = range(8)
-KIND_DECODE, KIND_PREFILL, KIND_MIXED = 0, 1, 2
+KIND_DECODE, KIND_PREFILL, KIND_MIXED, KIND_DENSE = 0, 1, 2, 3
 DTYPE_BF16 = 0
-_KINDS = {"decode": KIND_DECODE, "prefill": KIND_PREFILL, "mixed": KIND_MIXED}
+_KINDS = {"decode": KIND_DECODE, "prefill": KIND_PREFILL, "mixed": KIND_MIXED, "dense": KIND_DENSE}
 
 STATUS_NAMES = {OK: "PKV_OK", E_INVALID: "PKV_E_INVALID", E_UNSUPPORTED: "PKV_E_UNSUPPORTED",
                 E_WORKSPACE: "PKV_E_WORKSPACE", E_CAPACITY: "PKV_E_CAPACITY",
@@ -81,6 +81,14 @@ def _load():
         "pkv_run_append": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
         "pkv_context_only_views": (C.c_int, [C.c_int32, C.c_int32] + [P(C.c_int32)] * 9),
+        "pkv_dense_plan_create": (C.c_int, [C.c_void_p, C.c_int32] + [P(C.c_int32)] * 4
+                                  + [P(C.c_void_p), P(C.c_size_t)]),
+        "pkv_dense_plan_update": (C.c_int, [C.c_void_p, C.c_int32] + [P(C.c_int32)] * 4
+                                  + [P(C.c_size_t)]),
+        "pkv_dense_gather": (C.c_int, [C.c_void_p] * 6 + [C.c_int32, C.c_void_p, C.c_size_t,
+                                                         C.c_void_p]),
+        "pkv_dense_run": (C.c_int, [C.c_void_p] * 5 + [C.c_void_p, C.c_void_p, C.c_size_t,
+                                                      C.c_void_p]),
         "pkv_timing_enable": (C.c_int, [C.c_void_p, C.c_int32]),
         "pkv_timing_read": (C.c_int, [C.c_void_p, P(C.c_double), P(C.c_int64)]),
         "pkv_last_error": (C.c_char_p, []),
@@ -98,6 +106,7 @@ EXPORTED = ("pkv_plan_params_init", "pkv_plan_create", "pkv_plan_update", "pkv_p
             "pkv_plan_decode_tiles", "pkv_plan_prefill_tiles", "pkv_plan_merges",
             "pkv_plan_write_slots", "pkv_plan_permutation", "pkv_plan_info", "pkv_plan_upload",
             "pkv_run", "pkv_append_kv", "pkv_run_append", "pkv_context_only_views",
+            "pkv_dense_plan_create", "pkv_dense_plan_update", "pkv_dense_gather", "pkv_dense_run",
             "pkv_timing_enable", "pkv_timing_read",
             "pkv_last_error", "pkv_version")
 
@@ -185,7 +194,7 @@ class Plan:
         v = (C.c_int64 * 16)()
         _check(_lib.pkv_plan_info(self._h, v))
         keys = ["total_q", "batch", "decode_rows", "prompt_rows", "chunk_pages", "partial_slots",
-                "meta_bytes", "workspace_bytes", "num_cus"]
+                "meta_bytes", "workspace_bytes", "num_cus", "total_k"]
         return {k: int(v[i]) for i, k in enumerate(keys)}
 
 
@@ -297,6 +306,79 @@ def append_kv(plan: Plan, k_new, v_new, kv_cache_layer, workspace, stream=None):
 
 
 TIMING_KINDS = ("append", "decode", "merge", "prefill")
+
+
+def dense_plan_create(params: PlanParams, cu_q, cu_k, paged_kv_indptr=None,
+                      paged_kv_indices=None) -> Plan:
+    """pkv_dense_plan_create: rows of contiguous [prefix | fresh] K/V at cu_k
+    offsets, queries at cu_q offsets; the optional page table lets
+    dense_gather copy each row's prefix out of the pages (host only)."""
+    cq, ck, ind, idx = map(_i32, (cu_q, cu_k, paged_kv_indptr, paged_kv_indices))
+    batch = len(cq) - 1
+    if batch < 0 or len(ck) != batch + 1:
+        raise PkvError(1, "cu_q and cu_k need batch + 1 entries")
+    h, ws = C.c_void_p(), C.c_size_t()
+    _check(_lib.pkv_dense_plan_create(C.byref(params), batch, _ptr(cq), _ptr(ck), _ptr(ind),
+                                      _ptr(idx), C.byref(h), C.byref(ws)))
+    return Plan(h.value, ws.value, params, int(idx.max()) if idx is not None and idx.size else -1)
+
+
+def dense_plan_update(plan: Plan, cu_q, cu_k, paged_kv_indptr=None, paged_kv_indices=None) -> int:
+    """pkv_dense_plan_update: re-plan a dense handle; returns workspace bytes."""
+    cq, ck, ind, idx = map(_i32, (cu_q, cu_k, paged_kv_indptr, paged_kv_indices))
+    batch = len(cq) - 1
+    if batch < 0 or len(ck) != batch + 1:
+        raise PkvError(1, "cu_q and cu_k need batch + 1 entries")
+    ws = C.c_size_t()
+    _check(_lib.pkv_dense_plan_update(plan.handle, batch, _ptr(cq), _ptr(ck), _ptr(ind), _ptr(idx),
+                                      C.byref(ws)))
+    plan.ws_bytes = ws.value
+    plan.max_page_id = int(idx.max()) if idx is not None and idx.size else -1
+    return ws.value
+
+
+def _check_dense_sizes(plan: Plan, **tensors):
+    pp = plan.params
+    info = plan.info()
+    T, K = info["total_q"], info["total_k"]
+    row_q, row_k = pp.num_qo_heads * pp.head_dim, pp.num_kv_heads * pp.head_dim
+    want = {"q": T * row_q, "out": T * row_q, "lse": T * pp.num_qo_heads, "k": K * row_k,
+            "v": K * row_k, "k_fresh": T * row_k, "v_fresh": T * row_k, "k_out": K * row_k,
+            "v_out": K * row_k}
+    for name, t in tensors.items():
+        if t is not None and t.numel() != want[name]:
+            raise ValueError(f"{name} has {t.numel()} elements; the plan needs {want[name]}")
+
+
+def dense_gather(plan: Plan, kv_cache_layer, k_fresh, v_fresh, k_out, v_out, workspace,
+                 with_prefix=True, stream=None):
+    """pkv_dense_gather: fill k_out / v_out with each row's prefix (from the
+    pages, if with_prefix) and its fresh K/V."""
+    import torch
+    _check_dense_sizes(plan, k_fresh=k_fresh, v_fresh=v_fresh, k_out=k_out, v_out=v_out)
+    if with_prefix:
+        pp = plan.params
+        page = 2 * pp.page_size * pp.num_kv_heads * pp.head_dim
+        if kv_cache_layer is None or plan.max_page_id >= kv_cache_layer.numel() // page:
+            raise ValueError("kv_cache_layer does not hold the plan's pages")
+    _check(_lib.pkv_dense_gather(plan.handle, _dev(kv_cache_layer, "kv_cache_layer", torch.bfloat16),
+                                 _dev(k_fresh, "k_fresh", torch.bfloat16),
+                                 _dev(v_fresh, "v_fresh", torch.bfloat16),
+                                 _dev(k_out, "k_out", torch.bfloat16),
+                                 _dev(v_out, "v_out", torch.bfloat16), int(bool(with_prefix)),
+                                 _dev(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def dense_run(plan: Plan, q, k, v, out, workspace, lse=None, stream=None):
+    """pkv_dense_run: attention over contiguous [prefix | fresh] K/V."""
+    import torch
+    _check_dense_sizes(plan, q=q, k=k, v=v, out=out, lse=lse)
+    _check(_lib.pkv_dense_run(plan.handle, _dev(q, "q", torch.bfloat16),
+                              _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
+                              _dev(out, "out", torch.bfloat16), _dev(lse, "lse", torch.float32),
+                              _dev(workspace, "workspace"),
+                              workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def context_only_views(page_size, paged_kv_indptr, paged_kv_indices, paged_kv_last_page_len,
