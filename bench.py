@@ -62,6 +62,9 @@ DESCR = {
     "gqa_decode_context_only": "context-only decode over the gqa_decode rows: each row's appended "
                                "token dropped by context_only_views, one query per row attending "
                                "to the stored kv_len - 1 keys",
+    "tiny_decode_graph": "graph-static mode on the tiny decode rows (4 requests, Hq 4 / Hk 2, D 64, "
+                         "page 16, kv_len U[1,100]): re-plan and upload eagerly, then one replay "
+                         "of a captured append + decode + merge",
     "ragged_prefill_dense": "dense [prefix | fresh] mode over the ragged_prefill rows: prefixes "
                             "gathered from the pages once, each step's fresh K/V copied after "
                             "them, one dense varlen pass (contiguous K/V)",
@@ -147,6 +150,9 @@ class Runner:
         from paged_kv_attention_plan_amd import pkv
         self.torch, self.pkv = torch, pkv
         self.name = name
+        self.graph = name.endswith("_graph")
+        if self.graph:
+            name = name[:-len("_graph")]
         self.dense = name.endswith("_dense")
         if self.dense:
             name = name[:-len("_dense")]
@@ -171,23 +177,29 @@ class Runner:
         if self.dense:
             self._init_dense(dev)
             return
+        static = dict(static_max_batch=w.batch, static_max_tokens=w.total_q,
+                      static_max_page_entries=len(w.kv_indices)) if self.graph else {}
         self.params = pkv.plan_params(w.kind, num_qo_heads=w.num_qo_heads,
                                       num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
                                       page_size=w.page_size, max_pages=w.max_pages,
                                       causal=w.causal, window_left=w.window_left,
                                       max_prefill_rows=w.max_prefill_rows,
                                       decode_tiles_per_cu=tiles_per_cu,
-                                      decode_min_chunk_pages=min_chunk_pages)
+                                      decode_min_chunk_pages=min_chunk_pages, **static)
         self.plan = pkv.plan_create(self.params, self.qo, w.kv_indptr, w.kv_indices,
                                     w.last_page_len)
         self.ws = torch.empty(self.plan.ws_bytes, dtype=torch.uint8, device=dev)
         self.out = torch.empty_like(w.q)
         self.lse = torch.empty(w.total_q, w.num_qo_heads, dtype=torch.float32, device=dev)
-        self.append = w.kind == "decode" and name == "gqa_decode"
+        self.append = w.kind == "decode" and name in ("gqa_decode", "tiny_decode")
         self.step_descr = ("context_only_views + plan_update + upload + run (decode + split-KV "
                            "merge)" if self.context_only else
                            "plan_update + upload + append_kv + run (decode + split-KV merge)"
                            if self.append else "plan_update + upload + run")
+        if self.graph:
+            self.step_descr = ("plan_update + upload (eager) + replay of a captured append_kv + "
+                               "run (decode + split-KV merge)")
+            self._capture()
         self.work = work_of(w)
 
     def _init_dense(self, dev):
@@ -227,6 +239,25 @@ class Runner:
                            "prefixes gathered once before the timed steps")
         self.work = work_of(w)
 
+    def _eager_kernels(self):
+        w, pkv = self.w, self.pkv
+        if self.append:
+            pkv.append_kv(self.plan, w.k_new, w.v_new, w.cache, self.ws)
+        pkv.run(self.plan, w.q, w.cache, self.out, self.ws, lse=self.lse)
+
+    def _capture(self):
+        """Warm up, then capture the step's kernels (append_kv + run) of the
+        graph-static plan; step() replays them after the eager re-plan and
+        upload."""
+        torch, pkv = self.torch, self.pkv
+        pkv.plan_upload(self.plan, self.ws)
+        self._eager_kernels()
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g):
+            self._eager_kernels()
+        torch.cuda.synchronize()
+
     def gather_prefix_us(self, reps=10):
         """Event-timed µs of one full gather (prefixes from the pages + fresh rows)."""
         pkv, torch = self.pkv, self.torch
@@ -250,6 +281,11 @@ class Runner:
                              self.v_dense, self.ws, with_prefix=False)
             pkv.dense_run(self.plan, w.q, self.k_dense, self.v_dense, self.out, self.ws,
                           lse=self.lse)
+            return
+        if self.graph:
+            pkv.plan_update(self.plan, self.qo, w.kv_indptr, w.kv_indices, w.last_page_len)
+            pkv.plan_upload(self.plan, self.ws)
+            self.g.replay()
             return
         if self.context_only:  # the views are re-derived every step, as a serving loop would
             ptr, idx, lpl, _ = pkv.context_only_views(*self.views_in)
@@ -407,6 +443,11 @@ def cpu_baseline(runner, unit, budget_s=12.0):
 def secondary(name, dev, steps, warmup):
     r = Runner(name, dev)
     ms, _ = r.time_steps(steps, warmup)
+    if r.graph:  # no per-kernel events inside a replay: compare whole steps with eager ones
+        e = Runner(name[:-len("_graph")], dev)
+        e_ms, _ = e.time_steps(steps, warmup)
+        return {"workload": DESCR[name], "ms_per_step": round(ms, 4),
+                "eager_ms_per_step": round(e_ms, 4), "speedup": round(e_ms / ms, 3)}
     kt = r.kernel_times(steps)
     res = {"workload": DESCR[name], "ms_per_step": round(ms, 4),
            "kernels_us": {k: stats(v, 1e3) for k, v in kt.items() if v}}
@@ -511,7 +552,7 @@ def main():
     if not args.no_secondary:
         sec = []
         for name in ("long_decode", "ragged_prefill", "mixed_window", "gqa_decode_context_only",
-                     "ragged_prefill_dense"):
+                     "ragged_prefill_dense", "tiny_decode_graph"):
             if name != args.config:
                 sec.append(secondary(name, dev, max(5, args.steps // 5), 2))
         line["secondary"] = sec

@@ -110,6 +110,21 @@ typedef struct pkv_plan_params {
   int64_t max_pages;            /* pages in the layer slice; page ids must be below it */
   int32_t decode_tiles_per_cu;  /* split-KV target: at most this many decode tiles per CU; 0 = 32 */
   int32_t decode_min_chunk_pages; /* smallest split-KV chunk, in pages; 0 = 8 */
+  /* Graph-static mode (attn.wrappers: static buffers for graph capture, sized by
+   * batch_size / max_num_pages / max_total_tokens).  All three 0: off.  All three > 0:
+   * the workspace is laid out for at most static_max_batch rows, static_max_tokens
+   * query tokens and static_max_page_entries page-table entries, every re-plan must
+   * fit them (else PKV_E_CAPACITY), and pkv_plan_upload / pkv_append_kv / pkv_run
+   * launch the same kernels with the same arguments on every step, so a stream
+   * capture of pkv_append_kv / pkv_run can be replayed after each pkv_plan_update +
+   * pkv_plan_upload (the upload itself is not captured).  The kernels read the step's
+   * work counts from the uploaded workspace; grids are sized for the capacities.
+   * Buffers passed to captured calls keep their addresses across replays and hold
+   * static_max_tokens rows (only the step's rows are read or written).  Timing
+   * (pkv_timing_enable) must be off while capturing.  Not for dense plans. */
+  int32_t static_max_batch;
+  int32_t static_max_tokens;
+  int64_t static_max_page_entries;
 } pkv_plan_params;
 
 /* One unit of decode work: a row, a KV head and a contiguous key range.

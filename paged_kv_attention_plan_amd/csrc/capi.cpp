@@ -327,7 +327,7 @@ pkv_status check_run(const pkv_plan* plan, const void* q, const void* kv_cache_l
   if (st != PKV_OK) return st;
   if (plan->uploaded_ws != workspace)
     return fail(PKV_E_STATE, "the plan was not uploaded to this workspace (call pkv_plan_upload first)");
-  if (plan->d.total_q == 0) return PKV_OK;
+  if (plan->d.total_q == 0 && !plan->d.is_static) return PKV_OK;
   if (q == nullptr || kv_cache_layer == nullptr || out == nullptr)
     return fail(PKV_E_INVALID, "q, kv_cache_layer and out must not be NULL");
   if (!aligned16(q) || !aligned16(kv_cache_layer) || !aligned16(out) || !aligned16(workspace))
@@ -348,11 +348,16 @@ pkv_status run_impl(const pkv_plan* plan, const void* q, const void* kv_cache_la
   const int32_t* indices = reinterpret_cast<const int32_t*>(ws + d.ws.off_indices);
   float* part_o = reinterpret_cast<float*>(ws + d.ws.off_part_o);
   float* part_lse = reinterpret_cast<float*>(ws + d.ws.off_part_lse);
-  if (!d.decode_tiles.empty()) {
+  // A graph-static plan launches every kernel its kind can use, on grids sized
+  // for its capacities, and the kernels read the step's counts from the header.
+  const bool st = d.is_static;
+  const int64_t* counts = st ? reinterpret_cast<const int64_t*>(ws) : nullptr;
+  if (st ? d.caps.dec_tiles > 0 : !d.decode_tiles.empty()) {
     pkv::DecodeArgs a{};
     a.tiles = reinterpret_cast<const pkv::DecodeTileMeta*>(ws + d.ws.off_decode_tiles);
     a.rows = reinterpret_cast<const pkv::DecodeRowMeta*>(ws + d.ws.off_decode_rows);
-    a.n_tiles = (int32_t)d.decode_tiles.size();
+    a.n_tiles = (int32_t)(st ? d.caps.dec_tiles : (int64_t)d.decode_tiles.size());
+    a.counts = counts;
     a.indices = indices;
     a.q = static_cast<const uint16_t*>(q);
     a.cache = static_cast<const uint16_t*>(kv_cache_layer);
@@ -370,11 +375,14 @@ pkv_status run_impl(const pkv_plan* plan, const void* q, const void* kv_cache_la
     PKV_HIP(pkv::launch_decode(a, s));
     PKV_HIP(timing_mark(plan, s, kDecode, false));
   }
-  if (!d.merges.empty()) {
+  if (st ? d.caps.merges > 0 : !d.merges.empty()) {
     pkv::MergeArgs a{};
     a.merges = reinterpret_cast<const pkv_merge_entry*>(ws + d.ws.off_merges);
-    a.n_merges = (int32_t)d.merges.size();
-    a.max_chunks = d.max_merge_chunks;
+    a.n_merges = (int32_t)(st ? d.caps.merges : (int64_t)d.merges.size());
+    a.counts = counts;
+    // the one-wave-per-pair form serves any chunk count; a static launch must
+    // not depend on the step
+    a.max_chunks = st ? 0 : d.max_merge_chunks;
     a.part_o = part_o;
     a.part_lse = part_lse;
     a.out = static_cast<uint16_t*>(out);
@@ -386,10 +394,11 @@ pkv_status run_impl(const pkv_plan* plan, const void* q, const void* kv_cache_la
     PKV_HIP(pkv::launch_merge(a, s));
     PKV_HIP(timing_mark(plan, s, kMerge, false));
   }
-  if (!d.prefill_tiles.empty()) {
+  if (st ? d.caps.prefill_tiles > 0 : !d.prefill_tiles.empty()) {
     pkv::PrefillArgs a{};
     a.tiles = reinterpret_cast<const pkv_prefill_tile*>(ws + d.ws.off_prefill_tiles);
-    a.n_tiles = (int32_t)d.prefill_tiles.size();
+    a.n_tiles = (int32_t)(st ? d.caps.prefill_tiles : (int64_t)d.prefill_tiles.size());
+    a.counts = counts;
     a.indices = indices;
     a.q = static_cast<const uint16_t*>(q);
     a.cache = static_cast<const uint16_t*>(kv_cache_layer);
@@ -416,7 +425,7 @@ pkv_status pkv_run(const pkv_plan* plan, const void* q, const void* kv_cache_lay
                    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   pkv_status st = check_run(plan, q, kv_cache_layer, out, lse, workspace, workspace_bytes);
-  if (st != PKV_OK || plan->d.total_q == 0) return st;
+  if (st != PKV_OK || (plan->d.total_q == 0 && !plan->d.is_static)) return st;
   return run_impl(plan, q, kv_cache_layer, out, lse, workspace, stream);
 }
 
@@ -425,7 +434,7 @@ pkv_status pkv_run_append(const pkv_plan* plan, const void* q, const void* k_new
                           size_t workspace_bytes, void* stream) {
   g_err.clear();
   pkv_status st = check_run(plan, q, kv_cache_layer, out, lse, workspace, workspace_bytes);
-  if (st != PKV_OK || plan->d.total_q == 0) return st;
+  if (st != PKV_OK || (plan->d.total_q == 0 && !plan->d.is_static)) return st;
   if (k_new == nullptr || v_new == nullptr)
     return fail(PKV_E_INVALID, "k_new and v_new must not be NULL");
   if (!aligned16(k_new) || !aligned16(v_new))
@@ -447,14 +456,15 @@ pkv_status pkv_append_kv(const pkv_plan* plan, const void* k_new, const void* v_
   if (plan->uploaded_ws != workspace)
     return fail(PKV_E_STATE, "the plan was not uploaded to this workspace (call pkv_plan_upload first)");
   const pkv::PlanData& d = plan->d;
-  if (d.total_q == 0) return PKV_OK;
+  if (d.total_q == 0 && !d.is_static) return PKV_OK;
   if (k_new == nullptr || v_new == nullptr || kv_cache_layer == nullptr)
     return fail(PKV_E_INVALID, "k_new, v_new and kv_cache_layer must not be NULL");
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(kv_cache_layer))
     return fail(PKV_E_INVALID, "k_new, v_new and kv_cache_layer must be 16-byte aligned");
   pkv::AppendArgs a{};
   a.slots = reinterpret_cast<const int64_t*>(static_cast<char*>(workspace) + d.ws.off_slots);
-  a.n_tokens = d.total_q;
+  a.n_tokens = d.is_static ? (int32_t)d.caps.tokens : d.total_q;
+  a.counts = d.is_static ? reinterpret_cast<const int64_t*>(workspace) : nullptr;
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.cache = static_cast<uint16_t*>(kv_cache_layer);

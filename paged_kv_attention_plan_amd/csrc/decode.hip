@@ -35,7 +35,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tix = blockIdx.x * kWaves + wave;
-  if (tix >= a.n_tiles) return;
+  const int n_tiles = a.counts != nullptr ? (int)as_const4(a.counts)[0] : a.n_tiles;
+  if (tix >= n_tiles) return;
 
   // Plan metadata is read-only for the launch: scalar loads.
   const auto tp = as_const4(a.tiles + tix);

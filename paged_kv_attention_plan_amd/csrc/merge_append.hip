@@ -40,7 +40,8 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(MergeArgs a) {
   // pair index and this wave's rank among the pair's W waves
   const int pair = W == 1 ? blockIdx.x * kWaves + wave : blockIdx.x;
   const int rank = W == 1 ? 0 : wave;
-  if (pair >= a.n_merges * G) return;
+  const int n_merges = a.counts != nullptr ? (int)as_const4(a.counts)[1] : a.n_merges;
+  if (pair >= n_merges * G) return;
   const int mi = pair / G, h = pair - mi * G;
   const pkv_merge_entry e = a.merges[mi];
   const int n = e.n_chunks;
@@ -132,6 +133,7 @@ __global__ __launch_bounds__(64 * kWaves) void merge_kernel(MergeArgs a) {
 // trip; page_size is a power of two, so the slot splits by shift and mask.
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int t = blockIdx.x;
+  if (a.counts != nullptr && t >= (int)as_const4(a.counts)[4]) return;
   const int64_t slot = a.slots[t];
   const int ps = a.page_size;
   const int ps_log2 = __builtin_ctz(ps);

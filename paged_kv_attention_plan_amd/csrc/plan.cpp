@@ -137,6 +137,18 @@ pkv_status check_params(const pkv_plan_params& p, std::string& err) {
     err = "tuning knobs must be >= 0 (0 = default)";
     return PKV_E_INVALID;
   }
+  const bool any_static = p.static_max_batch != 0 || p.static_max_tokens != 0 ||
+                          p.static_max_page_entries != 0;
+  if (any_static) {
+    if (p.static_max_batch < 1 || p.static_max_tokens < 1 || p.static_max_page_entries < 1) {
+      err = "graph-static capacities must all be >= 1 (or all 0)";
+      return PKV_E_INVALID;
+    }
+    if (p.kind == PKV_KIND_DENSE) {
+      err = "dense plans have no graph-static mode";
+      return PKV_E_UNSUPPORTED;
+    }
+  }
   return PKV_OK;
 }
 
@@ -145,28 +157,68 @@ pkv_status check_params(const pkv_plan_params& p, std::string& err) {
 void layout_workspace(PlanData& plan) {
   const pkv_plan_params& P = plan.params;
   const int32_t g = plan.group;
+  const PlanData::Caps& c = plan.caps;
+  const bool st = plan.is_static;
+  // region sizes: this plan's counts, or the capacities of a graph-static plan
+  const size_t dec_rows = st ? c.dec_rows : plan.decode_rows.size();
+  const size_t dec_tiles = st ? c.dec_tiles : plan.decode_tile_meta.size();
+  const size_t merges = st ? c.merges : plan.merges.size();
+  const size_t pre_tiles = st ? c.prefill_tiles : plan.prefill_tiles.size();
+  const size_t indices = st ? c.indices : plan.indices.size();
+  const size_t slots = st ? c.tokens : plan.slots.size();
+  const size_t n_slots = st ? c.n_slots : (size_t)plan.n_slots;
   WorkspaceLayout& L = plan.ws;
-  size_t off = kAlign;  // first 256 bytes reserved
+  size_t off = kAlign;  // first 256 bytes: counts (and the upload's sequence number)
   L.off_dense_rows = off;
   off = align_up(off + plan.dense_rows.size() * sizeof(DenseRowMeta));
   L.off_decode_rows = off;
-  off = align_up(off + plan.decode_rows.size() * sizeof(DecodeRowMeta));
+  off = align_up(off + dec_rows * sizeof(DecodeRowMeta));
   L.off_decode_tiles = off;
-  off = align_up(off + plan.decode_tile_meta.size() * sizeof(DecodeTileMeta));
+  off = align_up(off + dec_tiles * sizeof(DecodeTileMeta));
   L.off_merges = off;
-  off = align_up(off + plan.merges.size() * sizeof(pkv_merge_entry));
+  off = align_up(off + merges * sizeof(pkv_merge_entry));
   L.off_prefill_tiles = off;
-  off = align_up(off + plan.prefill_tiles.size() * sizeof(pkv_prefill_tile));
+  off = align_up(off + pre_tiles * sizeof(pkv_prefill_tile));
   L.off_indices = off;
-  off = align_up(off + plan.indices.size() * sizeof(int32_t));
+  off = align_up(off + indices * sizeof(int32_t));
   L.off_slots = off;
-  off = align_up(off + plan.slots.size() * sizeof(int64_t));
+  off = align_up(off + slots * sizeof(int64_t));
   L.meta_bytes = off;
   L.off_part_o = off;
-  off = align_up(off + (size_t)plan.n_slots * g * P.head_dim * sizeof(float));
+  off = align_up(off + n_slots * g * P.head_dim * sizeof(float));
   L.off_part_lse = off;
-  off = align_up(off + (size_t)plan.n_slots * g * sizeof(float));
+  off = align_up(off + n_slots * g * sizeof(float));
   L.total_bytes = off;
+}
+
+// Capacities of a graph-static plan.  Decode tiles: the split-KV chunk grows
+// until the tiles fit tiles_per_cu * num_cus or every row is one chunk, so at
+// most max(budget, Hk * rows); and a chunk holds at least min_chunk_pages, so
+// at most Hk * (page entries / min_chunk_pages + rows) as well.  Each split
+// tile has one partial slot; a row splits into at most Hk merges.  Prefill
+// tiles: Hk per block of 128 / group tokens, at most
+// Hk * (ceil(tokens / block) + rows).
+PlanData::Caps static_caps(const pkv_plan_params& P, int32_t num_cus) {
+  PlanData::Caps c;
+  const int64_t Hk = P.num_kv_heads, g = P.num_qo_heads / P.num_kv_heads;
+  const int64_t B = P.static_max_batch, T = P.static_max_tokens;
+  const int64_t tiles_per_cu = P.decode_tiles_per_cu > 0 ? P.decode_tiles_per_cu : 32;
+  const int64_t min_chunk = P.decode_min_chunk_pages > 0 ? P.decode_min_chunk_pages : 8;
+  if (P.kind != PKV_KIND_PREFILL) {
+    c.dec_rows = B;
+    c.dec_tiles = std::min(std::max<int64_t>(tiles_per_cu * num_cus, Hk * B),
+                           Hk * ((P.static_max_page_entries + min_chunk - 1) / min_chunk + B));
+    c.merges = Hk * B;
+    c.n_slots = c.dec_tiles;
+  }
+  if (P.kind != PKV_KIND_DECODE) {
+    const int64_t bt = 128 / g;
+    const int64_t rows = P.kind == PKV_KIND_MIXED ? std::min<int64_t>(B, P.max_prefill_rows) : B;
+    c.prefill_tiles = Hk * ((T + bt - 1) / bt + rows);
+  }
+  c.indices = P.static_max_page_entries;
+  c.tokens = T;
+  return c;
 }
 
 pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
@@ -257,6 +309,15 @@ pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
     }
   }
   const int64_t total_q = decode_kind ? batch : (batch > 0 ? qo_indptr[batch] : 0);
+  const bool is_static = P.static_max_batch > 0;
+  if (is_static && (batch > P.static_max_batch || total_q > P.static_max_tokens ||
+                    nnz > P.static_max_page_entries)) {
+    err = "the step exceeds the graph-static capacities (batch " + std::to_string(batch) + " / " +
+          std::to_string(P.static_max_batch) + ", tokens " + std::to_string(total_q) + " / " +
+          std::to_string(P.static_max_tokens) + ", page entries " + std::to_string(nnz) + " / " +
+          std::to_string(P.static_max_page_entries) + ")";
+    return PKV_E_CAPACITY;
+  }
 
   PlanData plan;
   plan.params = P;
@@ -390,6 +451,18 @@ pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
   make_prefill_tiles(P, pre_rows, kv_len, q_len, q_start,
                      [&](int32_t r) { return kv_indptr[r]; }, plan.prefill_tiles);
 
+  if (is_static) {
+    plan.is_static = true;
+    plan.caps = static_caps(P, num_cus);
+    const PlanData::Caps& c = plan.caps;
+    if ((int64_t)plan.decode_rows.size() > c.dec_rows ||
+        (int64_t)plan.decode_tile_meta.size() > c.dec_tiles ||
+        (int64_t)plan.merges.size() > c.merges || plan.n_slots > c.n_slots ||
+        (int64_t)plan.prefill_tiles.size() > c.prefill_tiles) {
+      err = "internal: a graph-static plan outgrew its capacities";
+      return PKV_E_CAPACITY;
+    }
+  }
   layout_workspace(plan);
   out = std::move(plan);
   return PKV_OK;

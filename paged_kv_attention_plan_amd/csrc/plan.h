@@ -49,6 +49,12 @@ struct PlanData {
   std::vector<int32_t> indices;  // copy of paged_kv_indices
   std::vector<int64_t> slots;    // flat write slot per query token
   std::vector<int32_t> perm;     // mixed: prompt tokens first
+  // graph-static plans: the workspace is laid out for these capacities
+  bool is_static = false;
+  struct Caps {
+    int64_t dec_rows = 0, dec_tiles = 0, merges = 0, n_slots = 0, prefill_tiles = 0,
+            indices = 0, tokens = 0;
+  } caps;
   // dense plans
   bool dense = false;
   bool dense_pages = false;      // page table given: the gather may copy prefixes

@@ -93,6 +93,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2 * KBUF];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2 * VBUF];
 
+  if (a.counts != nullptr && (int64_t)blockIdx.x >= as_const4(a.counts)[2]) return;
   const pkv_prefill_tile* tp = a.tiles + blockIdx.x;
   const int hk = tp->kv_head;
   const int q_start = tp->q_start;

@@ -39,7 +39,9 @@ class PlanParams(C.Structure):
                 ("head_dim", C.c_int32), ("page_size", C.c_int32), ("causal", C.c_int32),
                 ("window_left", C.c_int32), ("dtype", C.c_int32), ("max_prefill_rows", C.c_int32),
                 ("num_cus", C.c_int32), ("max_pages", C.c_int64),
-                ("decode_tiles_per_cu", C.c_int32), ("decode_min_chunk_pages", C.c_int32)]
+                ("decode_tiles_per_cu", C.c_int32), ("decode_min_chunk_pages", C.c_int32),
+                ("static_max_batch", C.c_int32), ("static_max_tokens", C.c_int32),
+                ("static_max_page_entries", C.c_int64)]
 
 
 DECODE_TILE = np.dtype([("row", "<i4"), ("kv_head", "<i4"), ("kv_start", "<i4"), ("kv_end", "<i4"),
@@ -138,7 +140,8 @@ def version() -> str:
 
 def plan_params(kind="decode", *, num_qo_heads, num_kv_heads, head_dim, page_size, max_pages,
                 causal=True, window_left=-1, max_prefill_rows=0, num_cus=0,
-                decode_tiles_per_cu=0, decode_min_chunk_pages=0) -> PlanParams:
+                decode_tiles_per_cu=0, decode_min_chunk_pages=0, static_max_batch=0,
+                static_max_tokens=0, static_max_page_entries=0) -> PlanParams:
     p = PlanParams()
     _lib.pkv_plan_params_init(C.byref(p))
     p.kind = _KINDS[kind] if isinstance(kind, str) else int(kind)
@@ -146,6 +149,8 @@ def plan_params(kind="decode", *, num_qo_heads, num_kv_heads, head_dim, page_siz
     p.causal, p.window_left, p.dtype = int(bool(causal)), int(window_left), DTYPE_BF16
     p.max_prefill_rows, p.num_cus, p.max_pages = int(max_prefill_rows), int(num_cus), int(max_pages)
     p.decode_tiles_per_cu, p.decode_min_chunk_pages = int(decode_tiles_per_cu), int(decode_min_chunk_pages)
+    p.static_max_batch, p.static_max_tokens = int(static_max_batch), int(static_max_tokens)
+    p.static_max_page_entries = int(static_max_page_entries)
     return p
 
 
@@ -254,7 +259,8 @@ def _check_sizes(plan: Plan, kv_cache_layer, **tensors):
     """The C ABI takes raw pointers; make sure the tensors hold what the plan
     will touch before handing them over."""
     pp = plan.params
-    T = plan.info()["total_q"]
+    # graph-static plans take buffers sized for their capacity, whatever the step holds
+    T = pp.static_max_tokens if pp.static_max_batch > 0 else plan.info()["total_q"]
     want = {"q": T * pp.num_qo_heads * pp.head_dim, "out": T * pp.num_qo_heads * pp.head_dim,
             "lse": T * pp.num_qo_heads, "k_new": T * pp.num_kv_heads * pp.head_dim,
             "v_new": T * pp.num_kv_heads * pp.head_dim}

@@ -316,3 +316,67 @@ def test_empty_batch():
     plan = pkv.plan_create(p, np.zeros(1), np.zeros(1), np.zeros(0), np.zeros(0))
     assert plan.info()["total_q"] == 0 and len(plan.prefill_tiles()) == 0
     assert plan.ws_bytes > 0
+
+
+# ---- graph-static plans ----
+
+def _static_params(w, kind, B=16, T=1024, E=4096, max_pages=1000, **kw):
+    p = _params(w, kind, static_max_batch=B, static_max_tokens=T, static_max_page_entries=E, **kw)
+    p.max_pages = max_pages
+    return p
+
+
+@pytest.mark.parametrize("kind", ["decode", "prefill", "mixed"])
+def test_static_plan_layout_is_fixed_across_replans(kind):
+    """The workspace layout of a graph-static plan depends on its capacities
+    only, and its tiles are those of the ordinary plan of the same step."""
+    seeds = [81, 82, 83]
+    plan = sizes = None
+    for sd in seeds:
+        w = synth.random_case(sd, kind="decode" if kind == "decode" else "prefill", batch=6,
+                              page_size=4, head_dim=64, max_kv=120)
+        w.max_prefill_rows = 6
+        qo = None if kind == "decode" else w.qo_indptr
+        p = _static_params(w, kind)
+        if plan is None:
+            plan = pkv.plan_create(p, qo, w.kv_indptr, w.kv_indices, w.last_page_len)
+        else:
+            pkv.plan_update(plan, qo, w.kv_indptr, w.kv_indices, w.last_page_len)
+        info = plan.info()
+        now = (info["meta_bytes"], info["workspace_bytes"], plan.ws_bytes)
+        assert sizes is None or now == sizes
+        sizes = now
+        p0 = _params(w, kind)
+        p0.max_pages = 1000
+        ref = pkv.plan_create(p0, qo, w.kv_indptr, w.kv_indices, w.last_page_len)
+        assert np.array_equal(plan.decode_tiles(), ref.decode_tiles())
+        assert np.array_equal(plan.prefill_tiles(), ref.prefill_tiles())
+        assert np.array_equal(plan.merges(), ref.merges())
+        assert np.array_equal(plan.write_slots(), ref.write_slots())
+
+
+def test_static_plan_capacity_errors():
+    w = synth.random_case(84, kind="decode", batch=6, page_size=4, head_dim=64, max_kv=120)
+    with pytest.raises(pkv.PkvError, match="graph-static capacities"):
+        pkv.plan_create(_static_params(w, "decode", B=5), None, w.kv_indptr,
+                        w.kv_indices, w.last_page_len)
+    with pytest.raises(pkv.PkvError, match="graph-static capacities"):
+        pkv.plan_create(_static_params(w, "decode", E=3), None, w.kv_indptr,
+                        w.kv_indices, w.last_page_len)
+    plan = pkv.plan_create(_static_params(w, "decode"), None, w.kv_indptr,
+                           w.kv_indices, w.last_page_len)
+    w2 = synth.random_case(85, kind="decode", batch=20, page_size=4, head_dim=64, max_kv=120)
+    try:
+        pkv.plan_update(plan, None, w2.kv_indptr, w2.kv_indices, w2.last_page_len)
+        raise AssertionError("expected a capacity error")
+    except pkv.PkvError as e:
+        assert e.status == pkv.E_CAPACITY
+    # partial capacities and dense static plans are rejected
+    p = _params(w, "decode", static_max_batch=4)
+    with pytest.raises(pkv.PkvError, match="all be >= 1"):
+        pkv.plan_create(p, None, w.kv_indptr, w.kv_indices, w.last_page_len)
+    pd = pkv.plan_params("dense", num_qo_heads=4, num_kv_heads=2, head_dim=64, page_size=4,
+                         max_pages=10, num_cus=4, static_max_batch=1, static_max_tokens=1,
+                         static_max_page_entries=1)
+    with pytest.raises(pkv.PkvError, match="graph-static"):
+        pkv.dense_plan_create(pd, [0, 1], [0, 2])
