@@ -25,11 +25,16 @@ namespace {
 
 constexpr int kWaves = 4;  // wavefronts (tiles) per workgroup
 
+// Loads per iteration (each for K and V).  With 8 query heads per KV head the
+// accumulators take twice the registers, so the load buffers are halved to
+// keep every value in registers.
+constexpr int decode_loads(int G) { return G == 8 ? 2 : 4; }
+
 template <int D, int G, bool ONE_PAGE_PER_ITER>
 __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   constexpr int LPK = D / 8;       // lanes per key row
   constexpr int KPL = 64 / LPK;    // key rows per wave load
-  constexpr int U = 4;             // loads per iteration (each for K and V)
+  constexpr int U = decode_loads(G);  // loads per iteration (each for K and V)
   constexpr int KB = KPL * U;      // keys per iteration
 
   const int lane = threadIdx.x & 63;
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
 
 template <int D, int G>
 hipError_t launch_dg(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int KB = (64 / (D / 8)) * 4;
+  constexpr int KB = (64 / (D / 8)) * decode_loads(G);
   const dim3 grid((a.n_tiles + kWaves - 1) / kWaves), block(64 * kWaves);
   if (a.page_size >= KB)
     hipLaunchKernelGGL((decode_kernel<D, G, true>), grid, block, 0, stream, a);
