@@ -197,8 +197,22 @@ pkv_status pkv_plan_write_slots(const pkv_plan* plan, const int64_t** slots, int
 pkv_status pkv_plan_permutation(const pkv_plan* plan, const int32_t** perm, int32_t* n);
 /* Scalars: [0] total_q, [1] batch, [2] decode rows, [3] prompt rows, [4] split-KV chunk
  * pages, [5] partial slots, [6] metadata bytes, [7] workspace bytes, [8] num_cus used,
- * [9] dense key rows (cu_k[batch]; 0 for paged plans). */
+ * [9] dense key rows (cu_k[batch]; 0 for paged plans), and the byte offsets in the
+ * workspace of [10] the dense row table, [11] the decode row table, [12] the decode
+ * tiles, [13] the merge entries, [14] the prefill tiles, [15] the page-index copy. */
 pkv_status pkv_plan_info(const pkv_plan* plan, int64_t info[16]);
+
+/* Write the metadata image pkv_plan_upload copies into the workspace (its first
+ * pkv_plan_info[6] bytes) into host memory dst of `bytes` bytes, for inspection or
+ * for a caller's own copy: an int64 header [decode tiles, merges, prefill tiles,
+ * page indices, write slots, partial slots, query tokens, rows], then the regions
+ * at the offsets pkv_plan_info reports (16-byte decode tiles
+ * {int32 row, int16 kv_head, int16 chunk, int32 kv_start, int32 kv_end} and 32-byte
+ * decode rows {page_base, q_index, kv_len, first partial slot or -1, chunks, 3 pad};
+ * 32-byte dense rows {cu_k, cu_q, prefix, fresh, page_base, 3 pad}; merge entries and
+ * prefill tiles as declared above; int32 page indices; int64 write slots).  Host only.
+ * PKV_E_WORKSPACE if bytes is too small. */
+pkv_status pkv_plan_metadata(const pkv_plan* plan, void* dst, size_t bytes);
 
 /* Copy the plan's metadata into the head of `workspace` (device memory of at least
  * the plan's workspace_bytes), enqueued on `stream` (a hipStream_t; NULL = the null

@@ -232,6 +232,16 @@ pkv_status pkv_plan_write_slots(const pkv_plan* plan, const int64_t** slots, int
   return PKV_OK;
 }
 
+pkv_status pkv_plan_metadata(const pkv_plan* plan, void* dst, size_t bytes) {
+  g_err.clear();
+  if (plan == nullptr || dst == nullptr) return fail(PKV_E_INVALID, "NULL argument");
+  if (bytes < plan->d.ws.meta_bytes)
+    return fail(PKV_E_WORKSPACE, "the metadata image needs " +
+                                     std::to_string(plan->d.ws.meta_bytes) + " bytes");
+  pkv::serialize_meta(plan->d, dst);
+  return PKV_OK;
+}
+
 pkv_status pkv_plan_permutation(const pkv_plan* plan, const int32_t** perm, int32_t* n) {
   if (plan == nullptr || perm == nullptr || n == nullptr) return fail(PKV_E_INVALID, "NULL argument");
   *perm = plan->d.perm.data();
@@ -253,6 +263,12 @@ pkv_status pkv_plan_info(const pkv_plan* plan, int64_t info[16]) {
   info[7] = (int64_t)d.ws.total_bytes;
   info[8] = d.num_cus;
   info[9] = d.total_k;
+  info[10] = (int64_t)d.ws.off_dense_rows;
+  info[11] = (int64_t)d.ws.off_decode_rows;
+  info[12] = (int64_t)d.ws.off_decode_tiles;
+  info[13] = (int64_t)d.ws.off_merges;
+  info[14] = (int64_t)d.ws.off_prefill_tiles;
+  info[15] = (int64_t)d.ws.off_indices;
   return PKV_OK;
 }
 

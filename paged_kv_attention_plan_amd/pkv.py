@@ -82,6 +82,7 @@ def _load():
                                     C.c_size_t, C.c_void_p]),
         "pkv_run_append": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+        "pkv_plan_metadata": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t]),
         "pkv_context_only_views": (C.c_int, [C.c_int32, C.c_int32] + [P(C.c_int32)] * 9),
         "pkv_dense_plan_create": (C.c_int, [C.c_void_p, C.c_int32] + [P(C.c_int32)] * 4
                                   + [P(C.c_void_p), P(C.c_size_t)]),
@@ -106,7 +107,8 @@ def _load():
 _lib = _load()
 EXPORTED = ("pkv_plan_params_init", "pkv_plan_create", "pkv_plan_update", "pkv_plan_destroy",
             "pkv_plan_decode_tiles", "pkv_plan_prefill_tiles", "pkv_plan_merges",
-            "pkv_plan_write_slots", "pkv_plan_permutation", "pkv_plan_info", "pkv_plan_upload",
+            "pkv_plan_write_slots", "pkv_plan_permutation", "pkv_plan_info", "pkv_plan_metadata",
+            "pkv_plan_upload",
             "pkv_run", "pkv_append_kv", "pkv_run_append", "pkv_context_only_views",
             "pkv_dense_plan_create", "pkv_dense_plan_update", "pkv_dense_gather", "pkv_dense_run",
             "pkv_timing_enable", "pkv_timing_read",
@@ -195,11 +197,20 @@ class Plan:
     def permutation(self):
         return self._arr(_lib.pkv_plan_permutation, np.dtype("<i4"))
 
+    def metadata(self) -> np.ndarray:
+        """pkv_plan_metadata: the bytes the upload puts at the head of the workspace."""
+        n = self.info()["meta_bytes"]
+        buf = np.zeros(n, dtype=np.uint8)
+        _check(_lib.pkv_plan_metadata(self._h, buf.ctypes.data_as(C.c_void_p), n))
+        return buf
+
     def info(self) -> dict:
         v = (C.c_int64 * 16)()
         _check(_lib.pkv_plan_info(self._h, v))
         keys = ["total_q", "batch", "decode_rows", "prompt_rows", "chunk_pages", "partial_slots",
-                "meta_bytes", "workspace_bytes", "num_cus", "total_k"]
+                "meta_bytes", "workspace_bytes", "num_cus", "total_k", "off_dense_rows",
+                "off_decode_rows", "off_decode_tiles", "off_merges", "off_prefill_tiles",
+                "off_indices"]
         return {k: int(v[i]) for i, k in enumerate(keys)}
 
 

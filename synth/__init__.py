@@ -86,13 +86,15 @@ def _normals(gen: torch.Generator, shape, device) -> torch.Tensor:
 def from_lengths(name, kind, kv_len, q_len, *, num_qo_heads, num_kv_heads, head_dim, page_size,
                  causal=True, window_left=-1, pool_pages=None, rng=None, seed=0, device="cpu",
                  stale="zero", new_tokens=False, max_prefill_rows=0, gen=None,
-                 page_order="random") -> Workload:
+                 page_order="random", layout_only=False) -> Workload:
     """Lay rows of the given lengths out in a page pool and fill it.
 
     kv_len counts every token of the row, including the ones queried this step
     (those sit at the end: [cached prefix | fresh tokens]).  stale="zero"|"nan"
     selects what unused pages and slots past the last token hold.
     page_order: "random" (seeded permutation of the pool) or "sequential".
+    layout_only: the page table and lengths only (q, cache empty), e.g. for
+    planner checks at full size; the page ids are those of the full workload.
     """
     kv_len = np.asarray(kv_len, dtype=np.int64)
     q_len = np.asarray(q_len, dtype=np.int64)
@@ -114,6 +116,13 @@ def from_lengths(name, kind, kv_len, q_len, *, num_qo_heads, num_kv_heads, head_
     qo_indptr[1:] = np.cumsum(q_len)
     last_page_len = (((kv_len - 1) % ps) + 1).astype(np.int32)
 
+    if layout_only:
+        empty = torch.empty(0, dtype=torch.bfloat16)
+        return Workload(name=name, kind=kind, num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads,
+                        head_dim=head_dim, page_size=ps, causal=causal, window_left=window_left,
+                        max_pages=pool, kv_len=kv_len, q_len=q_len, qo_indptr=qo_indptr,
+                        kv_indptr=kv_indptr, kv_indices=ids, last_page_len=last_page_len,
+                        q=empty, cache=empty, max_prefill_rows=max_prefill_rows, seed=seed)
     gen = gen if gen is not None else torch.Generator(device=device).manual_seed(seed)
     T = int(qo_indptr[-1])
     q = _normals(gen, (T, num_qo_heads, head_dim), device)
@@ -147,7 +156,7 @@ def from_lengths(name, kind, kv_len, q_len, *, num_qo_heads, num_kv_heads, head_
 
 
 def make_workload(name: str, *, seed: Optional[int] = None, device="cpu", stale="zero",
-                  scale_rows: Optional[int] = None) -> Workload:
+                  scale_rows: Optional[int] = None, layout_only: bool = False) -> Workload:
     """One of the five named workloads.
 
     Default seed is 1000 + (1-based position in CONFIG_NAMES).  scale_rows, when
@@ -158,7 +167,7 @@ def make_workload(name: str, *, seed: Optional[int] = None, device="cpu", stale=
     seed = 1000 + k if seed is None else seed
     rng = np.random.default_rng(seed)
     gen = torch.Generator(device=device).manual_seed(seed)
-    common = dict(rng=rng, seed=seed, device=device, stale=stale, gen=gen)
+    common = dict(rng=rng, seed=seed, device=device, stale=stale, gen=gen, layout_only=layout_only)
 
     def cut(*arrs):
         if scale_rows is None:
