@@ -126,3 +126,15 @@ def test_captured_step_replays_with_new_plans(pkv, gpu, kind, seeds):
                                         num_kv_heads=hk, qo_indptr=qo(w), causal=True,
                                         window_left=-1)
         compare(g_out, g_lse, ref_o, ref_l, f"graph {kind} step {i}")
+
+    # an empty step: every captured kernel runs and finds no work
+    say(f"case graph {kind} empty step")
+    empty = np.zeros(0, dtype=np.int32)
+    pkv.plan_update(plan, None if kind == "decode" else np.zeros(1, np.int32),
+                    np.zeros(1, np.int32), empty, empty)
+    pkv.plan_upload(plan, ws)
+    out.fill_(7.0)
+    before = cache.clone()
+    g.replay()
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()) and torch.equal(cache.view(torch.int16), before.view(torch.int16))
