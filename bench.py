@@ -18,8 +18,9 @@ under "secondary".
 Besides the contract fields the line carries, per kernel kind, the mean and
 p10 / median / p90 of the event-timed launch durations; the host time of
 pkv_plan_update and the device time of the metadata upload, measured apart
-from the step; and measured ceilings of this GPU (a 2 GiB device copy and a
-bf16 GEMM) as context for the spec peaks.
+from the step; and measured ceilings of this GPU (a 2 GiB device copy, a
+bf16 GEMM, a register-only bf16 MFMA loop and a 2 GiB streaming read) as
+context for the spec peaks.
 
 Prints ONE JSON line.
 """
@@ -397,9 +398,60 @@ def ceilings(dev):
     gemm_tfs = 2 * m ** 3 / (min(best[1:]) * 1e-3) / 1e12
     del a, b
     torch.cuda.empty_cache()
-    return {"copy_GBps": round(copy_gbs, 1), "bf16_gemm_TFLOPs": round(gemm_tfs, 1),
-            "copy": "torch copy_ of 2 GiB, read + write bytes, best of 5",
-            "gemm": "torch.mm bf16 8192 x 8192 x 8192, best of 5"}
+    res = {"copy_GBps": round(copy_gbs, 1), "bf16_gemm_TFLOPs": round(gemm_tfs, 1),
+           "copy": "torch copy_ of 2 GiB, read + write bytes, best of 5",
+           "gemm": "torch.mm bf16 8192 x 8192 x 8192, best of 5"}
+    res.update(probe_ceilings(dev))
+    return res
+
+
+def probe_ceilings(dev):
+    """The two rates the attention kernels are bound by, from the probe
+    library built beside libpkv.so: a register-only bf16 MFMA loop
+    (v_mfma_f32_32x32x16_bf16, 4096 workgroups of 4 waves, 2048 rounds of four
+    independent products each) and a streaming read of 2 GiB (512 workgroups
+    of 256 threads, four 16-byte non-temporal loads in flight per thread: the
+    best of a sweep of launch shapes), each the best of 5 launches after
+    warm-up launches that bring the clocks up."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "paged_kv_attention_plan_amd", "libpkv_ceilings.so")
+    if not os.path.exists(path):
+        return {"probes": "libpkv_ceilings.so not built"}
+    lib = ctypes.CDLL(path)
+    lib.pkv_ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.pkv_ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_void_p]
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    blocks, iters, read_blocks = 4096, 2048, 512
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+
+    def best_ms(launch, warm=1):
+        t = []
+        for _ in range(warm + 5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if launch() != 0:
+                raise RuntimeError("probe launch failed")
+            e1.record(stream)
+            e1.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return min(t[warm:])
+
+    ms = best_ms(lambda: lib.pkv_ceiling_mfma(ctypes.c_void_p(sink.data_ptr()), blocks, iters, sh),
+                 warm=3)
+    mfma_tfs = blocks * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
+    nbytes = 2 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
+    ms = best_ms(lambda: lib.pkv_ceiling_read(ctypes.c_void_p(src.data_ptr()), nbytes,
+                                              ctypes.c_void_p(sink.data_ptr()), read_blocks, sh))
+    read_gbs = nbytes / (ms * 1e-3) / 1e9
+    del src, sink
+    torch.cuda.empty_cache()
+    return {"mfma_loop_TFLOPs": round(mfma_tfs, 1), "read_GBps": round(read_gbs, 1),
+            "mfma_loop": "register-only v_mfma_f32_32x32x16_bf16 loop, 16384 waves, best of 5",
+            "read": "streaming read of 2 GiB, 512 x 256 threads, 4 x 16-byte loads in flight, best of 5"}
 
 
 def cpu_baseline(runner, unit, budget_s=12.0):

@@ -1,4 +1,6 @@
-"""Build libpkv.so (host planner + C ABI + gfx950 kernels) in-tree with hipcc.
+"""Build libpkv.so (host planner + C ABI + gfx950 kernels) in-tree with hipcc,
+and libpkv_ceilings.so, the benchmark's measurement probes (a bf16 MFMA loop
+and a streaming read), which nothing on the attention path uses.
 
     python -m paged_kv_attention_plan_amd.build
 
@@ -20,9 +22,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
+CEIL_LIB = os.path.join(PKG, "libpkv_ceilings.so")
 ARCH = "gfx950"
 
 SOURCES = ["plan.cpp", "capi.cpp", "decode.hip", "merge_append.hip", "prefill.hip"]
+CEIL_SOURCES = ["ceilings.hip"]
 
 
 def hipcc() -> str:
@@ -56,19 +60,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libpkv.so.  Returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"linking libpkv.so failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"linking {os.path.basename(lib)} failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link libpkv.so and libpkv_ceilings.so.  Returns
+    the path of libpkv.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CEIL_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in CEIL_SOURCES], CEIL_LIB, verbose)
     return LIB
 
 
