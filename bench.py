@@ -145,7 +145,7 @@ def work_of(w):
 class Runner:
     """Holds the device buffers and the plan for one workload."""
 
-    def __init__(self, name, dev, tiles_per_cu=0, min_chunk_pages=0):
+    def __init__(self, name, dev, waves_per_cu=0, min_chunk_pages=0):
         import torch
         import synth
         from paged_kv_attention_plan_amd import pkv
@@ -185,7 +185,7 @@ class Runner:
                                       page_size=w.page_size, max_pages=w.max_pages,
                                       causal=w.causal, window_left=w.window_left,
                                       max_prefill_rows=w.max_prefill_rows,
-                                      decode_tiles_per_cu=tiles_per_cu,
+                                      decode_waves_per_cu=waves_per_cu,
                                       decode_min_chunk_pages=min_chunk_pages, **static)
         self.plan = pkv.plan_create(self.params, self.qo, w.kv_indptr, w.kv_indices,
                                     w.last_page_len)
@@ -535,8 +535,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured copy / bf16 GEMM ceilings")
-    ap.add_argument("--tiles-per-cu", type=int, default=0,
-                    help="split-KV planner knob (0 = library default)")
+    ap.add_argument("--waves-per-cu", type=int, default=0,
+                    help="split-KV planner knob: decode waves per CU (0 = library default)")
     ap.add_argument("--min-chunk-pages", type=int, default=0,
                     help="split-KV planner knob (0 = library default)")
     ap.add_argument("--record-traffic", nargs=5,
@@ -556,7 +556,7 @@ def main():
     from paged_kv_attention_plan_amd import pkv  # noqa: F401  (fails loudly if not built)
     dev = torch.device("cuda:0")
 
-    r = Runner(args.config, dev, args.tiles_per_cu, args.min_chunk_pages)
+    r = Runner(args.config, dev, args.waves_per_cu, args.min_chunk_pages)
     ms, wall_ms = r.time_steps(args.steps, args.warmup)
     kt = r.kernel_times(args.steps)
     w = r.work

@@ -108,8 +108,10 @@ typedef struct pkv_plan_params {
   int32_t num_cus;              /* compute units the plan balances over; 0 = ask the current HIP
                                    device (the workspace page: plan size depends on the SM count) */
   int64_t max_pages;            /* pages in the layer slice; page ids must be below it */
-  int32_t decode_tiles_per_cu;  /* split-KV target: at most this many decode tiles per CU; 0 = 32 */
-  int32_t decode_min_chunk_pages; /* smallest split-KV chunk, in pages; 0 = 8 */
+  int32_t decode_waves_per_cu;  /* decode waves per CU the split-KV partition balances over
+                                   (workers = num_cus * this / num_kv_heads); 0 = 4 for
+                                   group 1, 2, 4 and 16 for group 8 */
+  int32_t decode_min_chunk_pages; /* smallest per-worker share of a step's pages; 0 = 8 */
   /* Graph-static mode (attn.wrappers: static buffers for graph capture, sized by
    * batch_size / max_num_pages / max_total_tokens).  All three 0: off.  All three > 0:
    * the workspace is laid out for at most static_max_batch rows, static_max_tokens
@@ -130,7 +132,12 @@ typedef struct pkv_plan_params {
 /* One unit of decode work: a row, a KV head and a contiguous key range.
  * The tile covers keys [kv_start, kv_end) of the row; out_slot < 0 means the tile
  * writes out/lse directly, else it writes split-KV partial number out_slot into
- * the workspace and a merge combines the partials. */
+ * the workspace and a merge combines the partials.  Decode work is partitioned
+ * over workers, each a group of num_kv_heads waves: a row's visible pages are
+ * cut, at page boundaries, into pieces that the same cut gives every KV head;
+ * the tiles of a piece are num_kv_heads consecutive entries (kv_head 0, 1, ...),
+ * and a worker runs consecutive pieces so that every worker gets about the same
+ * number of pages (attn.workspace: the plan depends on the CU count). */
 typedef struct pkv_decode_tile {
   int32_t row, kv_head, kv_start, kv_end;
   int32_t page_base;  /* paged_kv_indptr[row] */
@@ -195,20 +202,24 @@ pkv_status pkv_plan_write_slots(const pkv_plan* plan, const int64_t** slots, int
 /* Mixed step: packed q indices of the prompt tokens, prompt rows in ascending order
  * ("moved to the front", FlashInferMixedWrapper).  n = 0 for other kinds. */
 pkv_status pkv_plan_permutation(const pkv_plan* plan, const int32_t** perm, int32_t* n);
-/* Scalars: [0] total_q, [1] batch, [2] decode rows, [3] prompt rows, [4] split-KV chunk
- * pages, [5] partial slots, [6] metadata bytes, [7] workspace bytes, [8] num_cus used,
- * [9] dense key rows (cu_k[batch]; 0 for paged plans), and the byte offsets in the
- * workspace of [10] the dense row table, [11] the decode row table, [12] the decode
- * tiles, [13] the merge entries, [14] the prefill tiles, [15] the page-index copy. */
-pkv_status pkv_plan_info(const pkv_plan* plan, int64_t info[16]);
+/* Scalars: [0] total_q, [1] batch, [2] decode rows, [3] prompt rows, [4] decode worker
+ * capacity (pages plus per-piece costs of two pages each), [5] partial slots,
+ * [6] metadata bytes, [7] workspace bytes, [8] num_cus used, [9] dense key rows
+ * (cu_k[batch]; 0 for paged plans), the byte offsets in the workspace of [10] the dense
+ * row table, [11] the decode row table, [12] the decode pieces, [13] the merge entries,
+ * [14] the prefill tiles, [15] the page-index copy, [16] the decode worker table, and
+ * [17] the decode workers (the table has [17] + 1 entries). */
+pkv_status pkv_plan_info(const pkv_plan* plan, int64_t info[18]);
 
 /* Write the metadata image pkv_plan_upload copies into the workspace (its first
  * pkv_plan_info[6] bytes) into host memory dst of `bytes` bytes, for inspection or
- * for a caller's own copy: an int64 header [decode tiles, merges, prefill tiles,
+ * for a caller's own copy: an int64 header [decode pieces, merges, prefill tiles,
  * page indices, write slots, partial slots, query tokens, rows], then the regions
- * at the offsets pkv_plan_info reports (16-byte decode tiles
- * {int32 row, int16 kv_head, int16 chunk, int32 kv_start, int32 kv_end} and 32-byte
- * decode rows {page_base, q_index, kv_len, first partial slot or -1, chunks, 3 pad};
+ * at the offsets pkv_plan_info reports (16-byte decode pieces
+ * {int32 decode row, int32 piece index within the row, int32 kv_start, int32 kv_end};
+ * 32-byte decode rows {page_base, q_index, kv_len, first partial slot or -1, pieces,
+ * 3 pad}, a row's partial for KV head h and piece c at first slot + h * pieces + c;
+ * the int32 decode worker table, worker w running pieces [table[w], table[w + 1]);
  * 32-byte dense rows {cu_k, cu_q, prefix, fresh, page_base, 3 pad}; merge entries and
  * prefill tiles as declared above; int32 page indices; int64 write slots).  Host only.
  * PKV_E_WORKSPACE if bytes is too small. */

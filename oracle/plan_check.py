@@ -14,14 +14,17 @@ Two kinds of check:
 
 Policy (the same rules the header documents):
   decode rows   visible keys [lo, N-1]; pages fp = lo // ps .. lp = (N-1) // ps.
-                chunk = min_chunk_pages * 2^k, the smallest with
-                Hk * sum_r ceil(pages_r / chunk) <= tiles_per_cu * num_cus, or
-                the first reaching the longest row.  A row of v pages is cut into
-                n = ceil(v / chunk) chunks, chunk i holding pages
-                [floor(i*v/n), floor((i+1)*v/n)).  Rows sorted by visible pages
-                descending (ties: row index); per row chunk-major, head-minor.
-                Rows with more than one chunk get Hk * n_chunks consecutive
-                partial slots, head-major.
+                W = max(1, num_cus * waves_per_cu // Hk) workers (waves_per_cu
+                4 for group 1, 2, 4 and 16 for group 8 unless given).  Rows sorted by
+                visible pages descending (ties: row index) are poured, in that
+                order, into workers of capacity C: a piece of p pages costs
+                p + 2; a worker takes min(remaining pages of the row, C - used -
+                2) pages of the row when that is >= 1, else the next worker
+                starts.  C is the smallest value >= max(min_chunk_pages,
+                ceil(total / W)) + 2 (total = pages + 2 per row) whose pour
+                needs at most W workers.  Per row pieces in order, per piece
+                tiles head-minor.  Rows with more than one piece get
+                Hk * n_pieces consecutive partial slots, head-major.
   prefill rows  blocks of 128 // group query tokens; per block keys
                 [lo(first token), hi(last token)]; tiles sorted by key count
                 descending, ties by (row, block, head).
@@ -49,50 +52,72 @@ def split_rows(kind, layout, max_prefill_rows=0):
     return dec, pre
 
 
-def decode_policy(layout, rows, *, page_size, num_kv_heads, window_left, num_cus, qo_indptr,
-                  kv_indptr, tiles_per_cu=32, min_chunk_pages=8):
-    """Expected decode tiles and merges.
+def _pour(pages, cap, cost=2):
+    """Pieces (row position, first page offset, page count, worker) of pouring
+    rows of `pages` pages, in order, into workers of capacity `cap`."""
+    pieces, w, used = [], 0, 0
+    for i, v in enumerate(pages):
+        done = 0
+        while done < v:
+            if cap - used - cost < 1:
+                w, used = w + 1, 0
+            take = min(v - done, cap - used - cost)
+            pieces.append((i, done, take, w))
+            used += take + cost
+            done += take
+    return pieces
 
-    Returns (tiles, merges, chunk_pages, n_slots) with tiles as tuples
-    (row, kv_head, kv_start, kv_end, page_base, q_index, out_slot, kv_len) and
-    merges as (q_index, kv_head, slot_base, n_chunks).
+
+def decode_policy(layout, rows, *, page_size, num_kv_heads, window_left, num_cus, qo_indptr,
+                  kv_indptr, group, waves_per_cu=0, min_chunk_pages=8):
+    """Expected decode tiles, merges and worker table.
+
+    Returns (tiles, merges, capacity, n_slots, work) with tiles as tuples
+    (row, kv_head, kv_start, kv_end, page_base, q_index, out_slot, kv_len),
+    merges as (q_index, kv_head, slot_base, n_chunks) and work the first piece
+    of every used worker followed by the piece count.
     """
-    ps = page_size
+    ps, hk_n = page_size, num_kv_heads
+    wpc = waves_per_cu or (16 if group == 8 else 4)
+    W = max(1, num_cus * wpc // hk_n)
     info = {}
     for r in rows:
         n = layout[r].kv_len
         lo, _ = visible_keys(n - 1, n, True, window_left)
         fp, lp = lo // ps, (n - 1) // ps
         info[r] = (lo, fp, lp, lp - fp + 1)
-    chunk = min_chunk_pages
-    if rows:
-        longest = max(v[3] for v in info.values())
-        budget = tiles_per_cu * num_cus
-
-        def count(c):
-            return num_kv_heads * sum(-(-v[3] // c) for v in info.values())
-
-        while chunk < longest and count(chunk) > budget:
-            chunk *= 2
     order = sorted(rows, key=lambda r: (-info[r][3], r))
-    tiles, merges = [], []
-    slot = 0
-    for r in order:
+    pages = [info[r][3] for r in order]
+    total = sum(v + 2 for v in pages)
+    cap = max(min_chunk_pages, -(-total // W)) + 2
+    if pages:
+        while _pour(pages, cap)[-1][3] + 1 > W:
+            cap += 1
+    pieces = _pour(pages, cap)
+    n_pieces = [sum(1 for p in pieces if p[0] == i) for i in range(len(order))]
+    base, slot, merges = {}, 0, []
+    for i, r in enumerate(order):
+        if n_pieces[i] > 1:
+            base[i] = slot
+            for hk in range(hk_n):
+                merges.append((int(qo_indptr[r]), hk, slot + hk * n_pieces[i], n_pieces[i]))
+            slot += hk_n * n_pieces[i]
+    tiles, work, seen = [], [], {}
+    for k, (i, off, take, w) in enumerate(pieces):
+        while len(work) <= w:
+            work.append(k)
+        r = order[i]
         lo, fp, lp, vis = info[r]
         n = layout[r].kv_len
-        nch = -(-vis // chunk)
-        base = slot if nch > 1 else -1
-        for i in range(nch):
-            ks = max(lo, (fp + i * vis // nch) * ps)
-            ke = min(n, (fp + (i + 1) * vis // nch) * ps)
-            for hk in range(num_kv_heads):
-                out_slot = base + hk * nch + i if nch > 1 else -1
-                tiles.append((r, hk, ks, ke, int(kv_indptr[r]), int(qo_indptr[r]), out_slot, n))
-        if nch > 1:
-            for hk in range(num_kv_heads):
-                merges.append((int(qo_indptr[r]), hk, base + hk * nch, nch))
-            slot += num_kv_heads * nch
-    return tiles, merges, chunk, slot
+        c = seen.get(i, 0)
+        seen[i] = c + 1
+        ks = max(lo, (fp + off) * ps)
+        ke = min(n, (fp + off + take) * ps)
+        for hk in range(hk_n):
+            out_slot = base[i] + hk * n_pieces[i] + c if i in base else -1
+            tiles.append((r, hk, ks, ke, int(kv_indptr[r]), int(qo_indptr[r]), out_slot, n))
+    work.append(len(pieces))
+    return tiles, merges, cap, slot, work
 
 
 def prefill_policy(layout, rows, *, num_qo_heads, num_kv_heads, causal, window_left, qo_indptr,

@@ -249,15 +249,15 @@ pkv_status pkv_plan_permutation(const pkv_plan* plan, const int32_t** perm, int3
   return PKV_OK;
 }
 
-pkv_status pkv_plan_info(const pkv_plan* plan, int64_t info[16]) {
+pkv_status pkv_plan_info(const pkv_plan* plan, int64_t info[18]) {
   if (plan == nullptr || info == nullptr) return fail(PKV_E_INVALID, "NULL argument");
   const pkv::PlanData& d = plan->d;
-  for (int i = 0; i < 16; ++i) info[i] = 0;
+  for (int i = 0; i < 18; ++i) info[i] = 0;
   info[0] = d.total_q;
   info[1] = d.batch;
   info[2] = d.n_decode_rows;
   info[3] = d.n_prompt_rows;
-  info[4] = d.chunk_pages;
+  info[4] = d.worker_pages;
   info[5] = d.n_slots;
   info[6] = (int64_t)d.ws.meta_bytes;
   info[7] = (int64_t)d.ws.total_bytes;
@@ -269,6 +269,8 @@ pkv_status pkv_plan_info(const pkv_plan* plan, int64_t info[16]) {
   info[13] = (int64_t)d.ws.off_merges;
   info[14] = (int64_t)d.ws.off_prefill_tiles;
   info[15] = (int64_t)d.ws.off_indices;
+  info[16] = (int64_t)d.ws.off_decode_work;
+  info[17] = d.is_static ? d.caps.dec_workers : d.n_workers;
   return PKV_OK;
 }
 
@@ -368,12 +370,13 @@ pkv_status run_impl(const pkv_plan* plan, const void* q, const void* kv_cache_la
   // for its capacities, and the kernels read the step's counts from the header.
   const bool st = d.is_static;
   const int64_t* counts = st ? reinterpret_cast<const int64_t*>(ws) : nullptr;
-  if (st ? d.caps.dec_tiles > 0 : !d.decode_tiles.empty()) {
+  if (st ? d.caps.dec_workers > 0 : d.n_workers > 0) {
+    // a graph-static plan's worker table always has its capacity's entries
     pkv::DecodeArgs a{};
-    a.tiles = reinterpret_cast<const pkv::DecodeTileMeta*>(ws + d.ws.off_decode_tiles);
+    a.pieces = reinterpret_cast<const pkv::DecodePieceMeta*>(ws + d.ws.off_decode_tiles);
     a.rows = reinterpret_cast<const pkv::DecodeRowMeta*>(ws + d.ws.off_decode_rows);
-    a.n_tiles = (int32_t)(st ? d.caps.dec_tiles : (int64_t)d.decode_tiles.size());
-    a.counts = counts;
+    a.work = reinterpret_cast<const int32_t*>(ws + d.ws.off_decode_work);
+    a.n_workers = (int32_t)(st ? d.caps.dec_workers : (int64_t)d.n_workers);
     a.indices = indices;
     a.q = static_cast<const uint16_t*>(q);
     a.cache = static_cast<const uint16_t*>(kv_cache_layer);

@@ -1,10 +1,14 @@
 // Batched GQA decode over a paged KV cache (FlashInferDecodeWrapper.run on the
 // mstar attn.wrappers page; split-KV partials in the workspace, attn.workspace).
 //
-// One wavefront per tile = (row, KV head, contiguous key chunk).  A key row of
-// one KV head is head_dim bf16 = D*2 bytes, contiguous in the cache; it is
-// spread over LPK = D/8 lanes, 16 bytes each, so one wave-wide load fetches
-// KPL = 64/LPK whole key rows with fully used 16-byte lane accesses.  An
+// Work comes as a worker table: worker w is num_kv_heads wavefronts, one per KV
+// head, that run the key-range pieces [work[w], work[w + 1]) in order; the
+// planner gives every worker about the same number of pages, so the waves of a
+// launch finish together.  A piece is a contiguous key range of one row.
+//
+// A key row of one KV head is head_dim bf16 = D*2 bytes, contiguous in the
+// cache; it is spread over LPK = D/8 lanes, 16 bytes each, so one wave-wide load
+// fetches KPL = 64/LPK whole key rows with fully used 16-byte lane accesses.  An
 // iteration issues U such loads for K and U for V (KB = KPL*U keys) and the
 // next iteration's loads go out before the current one is computed.  K and V
 // are streamed once, so they are loaded non-temporal.
@@ -13,12 +17,15 @@
 // group's G query heads (bf16 dot2), then a DPP allreduce over its LPK lanes.
 // Softmax: the KPL lane groups of a wave each keep their own running max, sum
 // and output accumulator (fp32, in registers) over the keys they see; the
-// groups are combined once, at the end of the tile, by log-sum-exp.
+// groups are combined once, at the end of the piece, by log-sum-exp.  Only
+// blocks that cross a piece's first or last key mask keys.
 //
 // Memory traffic is one read of every visible K and V byte: the kernel is
 // bound by HBM bandwidth.
 #include "common.cuh"
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace pkv {
 namespace {
@@ -30,23 +37,17 @@ constexpr int kWaves = 4;  // wavefronts (tiles) per workgroup
 // keep every value in registers.
 constexpr int decode_loads(int G) { return G == 8 ? 2 : 4; }
 
+// One piece (keys [kv_start, kv_end) of one row) for KV head hk, by one wave.
 template <int D, int G, bool ONE_PAGE_PER_ITER>
-__global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_piece(const DecodeArgs& a, int piece, int hk, int lane) {
   constexpr int LPK = D / 8;       // lanes per key row
   constexpr int KPL = 64 / LPK;    // key rows per wave load
   constexpr int U = decode_loads(G);  // loads per iteration (each for K and V)
   constexpr int KB = KPL * U;      // keys per iteration
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tix = blockIdx.x * kWaves + wave;
-  const int n_tiles = a.counts != nullptr ? (int)as_const4(a.counts)[0] : a.n_tiles;
-  if (tix >= n_tiles) return;
-
   // Plan metadata is read-only for the launch: scalar loads.
-  const auto tp = as_const4(a.tiles + tix);
+  const auto tp = as_const4(a.pieces + piece);
   const int row_ref = tp->row;
-  const int hk = tp->kv_head;
   const int chunk = tp->chunk;
   const int ks = tp->kv_start;
   const int ke = tp->kv_end;
@@ -139,7 +140,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
     }
   };
 
-  auto compute = [&](const uint4 (&kk)[U], const uint4 (&vv)[U], int b) {
+  auto compute_blk = [&](const uint4 (&kk)[U], const uint4 (&vv)[U], int b, auto edge_c) {
+    constexpr bool kEdge = decltype(edge_c)::value;
     const int kb = kb0 + b * KB;
     float s[U][G];
 #pragma unroll
@@ -153,14 +155,15 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         s[u][h] = group_sum<LPK>(acc) * a.scale_log2;
       }
     }
-    const bool edge = kb < ks || kb + KB > ke;  // uniform: a chunk edge
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = kb + u * KPL + lk;
-      ok[u] = !edge || (j >= ks && j < ke);
+      ok[u] = !kEdge || (j >= ks && j < ke);
+      if constexpr (kEdge) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[u][h] = ok[u] ? s[u][h] : -INFINITY;
+        for (int h = 0; h < G; ++h) s[u][h] = ok[u] ? s[u][h] : -INFINITY;
+      }
     }
     // New running max per head; rescale what was accumulated so far.
 #pragma unroll
@@ -183,8 +186,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
       vf[2] = bf16_lo(vv[u].y); vf[3] = bf16_hi(vv[u].y);
       vf[4] = bf16_lo(vv[u].z); vf[5] = bf16_hi(vv[u].z);
       vf[6] = bf16_lo(vv[u].w); vf[7] = bf16_hi(vv[u].w);
+      if constexpr (kEdge) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vf[e] = ok[u] ? vf[e] : 0.f;  // stale slots may hold NaN
+        for (int e = 0; e < 8; ++e) vf[e] = ok[u] ? vf[e] : 0.f;  // stale slots may hold NaN
+      }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float p = fast_exp2(s[u][h] - m[h]);
@@ -193,6 +198,17 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
         for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vf[e], o[h][e]);
       }
     }
+  };
+  // A block that crosses the piece's first or last key masks per key; the
+  // others (all but at most two per piece) skip the masks.  Uniform branch.
+  // With 8 query heads per KV head the second copy of the block code would
+  // not fit the registers of two waves per SIMD: every block masks.
+  auto compute = [&](const uint4 (&kk)[U], const uint4 (&vv)[U], int b) {
+    const int kb = kb0 + b * KB;
+    if (G == 8 || kb < ks || kb + KB > ke)
+      compute_blk(kk, vv, b, std::true_type{});
+    else
+      compute_blk(kk, vv, b, std::false_type{});
   };
 
   // Two register buffers: one block's loads are in flight while the other is
@@ -259,10 +275,24 @@ __global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
   }
 }
 
+template <int D, int G, bool ONE_PAGE_PER_ITER>
+__global__ __launch_bounds__(64 * kWaves) void decode_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * kWaves + wave;  // global wave index
+  const int worker = gw / a.num_kv_heads;
+  if (worker >= a.n_workers) return;
+  const int hk = gw - worker * a.num_kv_heads;
+  const auto wp = as_const4(a.work + worker);
+  const int p0 = wp[0], p1 = wp[1];
+  for (int p = p0; p < p1; ++p) decode_piece<D, G, ONE_PAGE_PER_ITER>(a, p, hk, lane);
+}
+
 template <int D, int G>
 hipError_t launch_dg(const DecodeArgs& a, hipStream_t stream) {
   constexpr int KB = (64 / (D / 8)) * decode_loads(G);
-  const dim3 grid((a.n_tiles + kWaves - 1) / kWaves), block(64 * kWaves);
+  const int64_t waves = (int64_t)a.n_workers * a.num_kv_heads;
+  const dim3 grid((uint32_t)((waves + kWaves - 1) / kWaves)), block(64 * kWaves);
   if (a.page_size >= KB)
     hipLaunchKernelGGL((decode_kernel<D, G, true>), grid, block, 0, stream, a);
   else
@@ -284,7 +314,7 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  if (a.n_tiles <= 0) return hipSuccess;
+  if (a.n_workers <= 0) return hipSuccess;
   if (a.head_dim == 128) return launch_d<128>(a, stream);
   if (a.head_dim == 64) return launch_d<64>(a, stream);
   return hipErrorInvalidValue;

@@ -11,14 +11,10 @@
 namespace pkv {
 
 struct DecodeArgs {
-  const DecodeTileMeta* tiles;
+  const DecodePieceMeta* pieces;
   const DecodeRowMeta* rows;
-  int32_t n_tiles;
-  // Graph-static plans: the uploaded counts (workspace header, int64 [8]:
-  // decode tiles, merges, prefill tiles, indices, slots, partial slots,
-  // tokens, rows) replace the n_* arguments, and the grids are sized for the
-  // plan's capacities.  Null otherwise.
-  const int64_t* counts;
+  const int32_t* work;      // [n_workers + 1]: worker w runs pieces [work[w], work[w + 1])
+  int32_t n_workers;        // each worker is num_kv_heads waves, one per KV head
   const int32_t* indices;   // paged_kv_indices on the device
   const uint16_t* q;        // bf16 [total_q, Hq, D]
   const uint16_t* cache;    // bf16 [max_pages, 2, ps, Hk, D]
@@ -30,10 +26,16 @@ struct DecodeArgs {
   float scale_log2;         // log2(e) / sqrt(head_dim)
 };
 
+// Graph-static plans: `counts` points at the uploaded counts (workspace header,
+// int64 [8]: decode pieces, merges, prefill tiles, indices, slots, partial
+// slots, tokens, rows), which replace the n_* arguments; the grids are sized for
+// the plan's capacities.  Null otherwise.  (Decode needs no count: its grid is
+// the plan's workers and the uploaded worker table gives every worker its
+// range, empty for the unused ones.)
 struct MergeArgs {
   const pkv_merge_entry* merges;
   int32_t n_merges;
-  const int64_t* counts;    // as in DecodeArgs
+  const int64_t* counts;    // see above
   int32_t max_chunks;       // largest n_chunks of any entry
   const float* part_o;
   const float* part_lse;
@@ -45,7 +47,7 @@ struct MergeArgs {
 struct AppendArgs {
   const int64_t* slots;     // flat page * ps + offset per token
   int32_t n_tokens;
-  const int64_t* counts;    // as in DecodeArgs
+  const int64_t* counts;    // as in MergeArgs
   const uint16_t* k_new;    // bf16 [n_tokens, Hk, D]
   const uint16_t* v_new;
   uint16_t* cache;
@@ -55,7 +57,7 @@ struct AppendArgs {
 struct PrefillArgs {
   const pkv_prefill_tile* tiles;
   int32_t n_tiles;
-  const int64_t* counts;    // as in DecodeArgs
+  const int64_t* counts;    // as in MergeArgs
   const int32_t* indices;
   const uint16_t* q;
   const uint16_t* cache;

@@ -1,28 +1,30 @@
 // Device-side form of a plan's rows and tiles, as uploaded to the workspace.  The public
 // structs of pkv.h (pkv_decode_tile, pkv_merge_entry) stay the inspection view;
-// this form is what the decode kernel reads: a 16-byte tile plus a per-row
-// table, so the per-step upload is about half the size.
+// this form is what the decode kernel reads: 16-byte key-range pieces, a
+// per-row table and a per-worker piece range, so the per-step upload stays
+// small.
 #pragma once
 
 #include <cstdint>
 
 namespace pkv {
 
-// One decode row (a row with one query token), in decode-tile order.
+// One decode row (a row with one query token), in decode-piece order.
 struct DecodeRowMeta {
   int32_t page_base;  // paged_kv_indptr[row]
   int32_t q_index;    // token index into q / out / k_new / v_new
   int32_t kv_len;
   int32_t slot0;      // first partial slot of the row (-1: not split)
-  int32_t n_chunks;   // key chunks per KV head (1: not split)
+  int32_t n_chunks;   // pieces of the row, the same for every KV head (1: not split)
   int32_t pad[3];
 };
 
-// One decode tile: keys [kv_start, kv_end) of one KV head of one row.
-struct DecodeTileMeta {
+// One decode piece: keys [kv_start, kv_end) of one row, run by every wave of
+// a decode worker (one wave per KV head).  Worker w runs the pieces
+// [work[w], work[w + 1]) of the worker table in order.
+struct DecodePieceMeta {
   int32_t row;        // index into the DecodeRowMeta table
-  int16_t kv_head;
-  int16_t chunk;      // chunk index within the row
+  int32_t chunk;      // piece index within the row
   int32_t kv_start;
   int32_t kv_end;
 };
@@ -38,6 +40,6 @@ struct DenseRowMeta {
 
 static_assert(sizeof(DenseRowMeta) == 32, "dense rows are 32 bytes");
 static_assert(sizeof(DecodeRowMeta) == 32, "row table entries are 32 bytes");
-static_assert(sizeof(DecodeTileMeta) == 16, "decode tiles are 16 bytes");
+static_assert(sizeof(DecodePieceMeta) == 16, "decode pieces are 16 bytes");
 
 }  // namespace pkv

@@ -8,14 +8,19 @@
 // Tiling policy (ours; the pages leave it open):
 //  decode  A row's single query sits at position N-1 and sees keys [lo, N-1],
 //          lo = max(0, N-1-window_left) (or 0).  Its visible pages run from
-//          lo/ps to (N-1)/ps.  The split-KV chunk C (pages) is the smallest
-//          min_chunk_pages * 2^k for which Hk * sum_r ceil(pages_r / C) fits
-//          tiles_per_cu * num_cus, or the first that reaches the longest row.
-//          A row of v visible pages is cut into n = ceil(v / C) chunks of
-//          nearly equal size: chunk i holds pages [i*v/n, (i+1)*v/n) (floor),
-//          so no tile is a short remainder.  Rows are taken longest first
-//          (ties: lower row index); a row's tiles are chunk-major, KV-head-minor.  A row cut into n > 1 chunks owns
-//          Hk * n consecutive partial slots (head-major) and one merge per head.
+//          lo/ps to (N-1)/ps.  Decode work runs on W workers, each a group of
+//          Hk waves (one per KV head) that walk the same key ranges:
+//          W = max(1, floor(num_cus * waves_per_cu / Hk)), waves_per_cu 4 for
+//          group 1, 2, 4 and 16 for group 8 unless given.  A piece of p pages costs
+//          p + kPieceCost (its start-up and epilogue, in page-times).  Rows
+//          are taken longest first (ties: lower row index) and poured in that
+//          order into workers of capacity C: a worker takes as many of a row's
+//          pages as fit (at least one), closes once fewer than one page fits,
+//          and the row continues in the next worker.  C is the smallest value
+//          >= max(min_chunk_pages, ceil(total / W)) + kPieceCost, total the
+//          pages plus one piece cost per row, for which the pour uses at most
+//          W workers.  A row cut into n > 1 pieces owns Hk * n consecutive
+//          partial slots (head-major) and one merge per head.
 //  prefill Query tokens are taken in blocks of 128/group so a block fills the
 //          128 rows of a kernel tile; a block's keys are [lo of its first token,
 //          hi of its last token].  Tiles are ordered by key count, largest first
@@ -33,6 +38,49 @@ namespace {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Start-up and epilogue of a decode piece, in page-times (the time a wave
+// takes to stream one page of its KV head): loading the piece's metadata, its
+// query and first keys, and combining and storing its result.
+constexpr int64_t kPieceCost = 2;
+
+// Decode workers of a plan: groups of Hk waves.  By default four waves per CU
+// (one four-wave workgroup each) for groups up to 4, where the kernel streams
+// HBM and one wave per SIMD keeps enough loads in flight; sixteen for group 8,
+// where the kernel is bound by its vector ALU and more, shorter pieces keep
+// every SIMD busy.  (Measured on MI355X over waves per CU 4, 8, 12 and 16.)
+int64_t decode_workers(const pkv_plan_params& P, int64_t num_cus) {
+  const int64_t g = P.num_qo_heads / P.num_kv_heads;
+  const int64_t waves_per_cu = P.decode_waves_per_cu > 0 ? P.decode_waves_per_cu
+                               : g == 8                  ? 16
+                                                         : 4;
+  return std::max<int64_t>(1, num_cus * waves_per_cu / P.num_kv_heads);
+}
+
+// Pour rows of `pages` (in order) into workers of capacity `cap`; emit(row
+// position, first page offset within the row, page count, worker) per piece.
+// Returns the number of workers used.
+template <class Emit>
+int64_t pour(const std::vector<int64_t>& pages, int64_t cap, Emit emit) {
+  int64_t w = 0, used = 0;
+  bool any = false;
+  for (size_t i = 0; i < pages.size(); ++i) {
+    for (int64_t done = 0; done < pages[i];) {
+      int64_t avail = cap - used - kPieceCost;
+      if (avail < 1) {
+        ++w;
+        used = 0;
+        avail = cap - kPieceCost;
+      }
+      const int64_t take = std::min(pages[i] - done, avail);
+      emit(i, done, take, w);
+      any = true;
+      used += take + kPieceCost;
+      done += take;
+    }
+  }
+  return any ? w + 1 : 0;
+}
 
 std::string fmt_row(const char* what, int64_t r) {
   return std::string(what) + " (row " + std::to_string(r) + ")";
@@ -133,7 +181,7 @@ pkv_status check_params(const pkv_plan_params& p, std::string& err) {
     err = "max_prefill_rows must be >= 0";
     return PKV_E_INVALID;
   }
-  if (p.decode_tiles_per_cu < 0 || p.decode_min_chunk_pages < 0) {
+  if (p.decode_waves_per_cu < 0 || p.decode_min_chunk_pages < 0) {
     err = "tuning knobs must be >= 0 (0 = default)";
     return PKV_E_INVALID;
   }
@@ -161,7 +209,8 @@ void layout_workspace(PlanData& plan) {
   const bool st = plan.is_static;
   // region sizes: this plan's counts, or the capacities of a graph-static plan
   const size_t dec_rows = st ? c.dec_rows : plan.decode_rows.size();
-  const size_t dec_tiles = st ? c.dec_tiles : plan.decode_tile_meta.size();
+  const size_t dec_pieces = st ? c.dec_pieces : plan.decode_pieces.size();
+  const size_t dec_work = plan.decode_work.size();  // capacity + 1 when graph-static
   const size_t merges = st ? c.merges : plan.merges.size();
   const size_t pre_tiles = st ? c.prefill_tiles : plan.prefill_tiles.size();
   const size_t indices = st ? c.indices : plan.indices.size();
@@ -174,7 +223,9 @@ void layout_workspace(PlanData& plan) {
   L.off_decode_rows = off;
   off = align_up(off + dec_rows * sizeof(DecodeRowMeta));
   L.off_decode_tiles = off;
-  off = align_up(off + dec_tiles * sizeof(DecodeTileMeta));
+  off = align_up(off + dec_pieces * sizeof(DecodePieceMeta));
+  L.off_decode_work = off;
+  off = align_up(off + dec_work * sizeof(int32_t));
   L.off_merges = off;
   off = align_up(off + merges * sizeof(pkv_merge_entry));
   L.off_prefill_tiles = off;
@@ -191,25 +242,22 @@ void layout_workspace(PlanData& plan) {
   L.total_bytes = off;
 }
 
-// Capacities of a graph-static plan.  Decode tiles: the split-KV chunk grows
-// until the tiles fit tiles_per_cu * num_cus or every row is one chunk, so at
-// most max(budget, Hk * rows); and a chunk holds at least min_chunk_pages, so
-// at most Hk * (page entries / min_chunk_pages + rows) as well.  Each split
-// tile has one partial slot; a row splits into at most Hk merges.  Prefill
+// Capacities of a graph-static plan.  Decode: W workers (fixed by the
+// parameters); every worker boundary cuts at most one row, so at most
+// rows + W - 1 pieces; a split row of n pieces owns Hk * n partial slots, so at
+// most Hk * (rows + W) slots; a row splits into at most Hk merges.  Prefill
 // tiles: Hk per block of 128 / group tokens, at most
 // Hk * (ceil(tokens / block) + rows).
 PlanData::Caps static_caps(const pkv_plan_params& P, int32_t num_cus) {
   PlanData::Caps c;
   const int64_t Hk = P.num_kv_heads, g = P.num_qo_heads / P.num_kv_heads;
   const int64_t B = P.static_max_batch, T = P.static_max_tokens;
-  const int64_t tiles_per_cu = P.decode_tiles_per_cu > 0 ? P.decode_tiles_per_cu : 32;
-  const int64_t min_chunk = P.decode_min_chunk_pages > 0 ? P.decode_min_chunk_pages : 8;
   if (P.kind != PKV_KIND_PREFILL) {
     c.dec_rows = B;
-    c.dec_tiles = std::min(std::max<int64_t>(tiles_per_cu * num_cus, Hk * B),
-                           Hk * ((P.static_max_page_entries + min_chunk - 1) / min_chunk + B));
+    c.dec_workers = decode_workers(P, num_cus);
+    c.dec_pieces = B + c.dec_workers;
     c.merges = Hk * B;
-    c.n_slots = c.dec_tiles;
+    c.n_slots = Hk * c.dec_pieces;
   }
   if (P.kind != PKV_KIND_DECODE) {
     const int64_t bt = 128 / g;
@@ -371,81 +419,89 @@ pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
       for (int32_t t = 0; t < q_len[r]; ++t) plan.perm.push_back(q_start[r] + t);
   }
 
-  // ---- decode tiles and split-KV chunks ----
-  const int32_t tiles_per_cu = P.decode_tiles_per_cu > 0 ? P.decode_tiles_per_cu : 32;
-  const int32_t min_chunk = P.decode_min_chunk_pages > 0 ? P.decode_min_chunk_pages : 8;
+  // ---- decode pieces, workers and split-KV partials ----
+  const int64_t min_chunk = P.decode_min_chunk_pages > 0 ? P.decode_min_chunk_pages : 8;
+  const int64_t W = decode_workers(P, num_cus);
   struct DecRow { int32_t r; int64_t lo, fp, lp, vis; };
   std::vector<DecRow> drows;
   drows.reserve(dec_rows.size());
-  int64_t longest = 0;
   for (int32_t r : dec_rows) {
     const int64_t n = kv_len[r];
     const int64_t lo = w < 0 ? 0 : std::max<int64_t>(0, n - 1 - w);
     const int64_t fp = lo / ps, lp = (n - 1) / ps;
     drows.push_back({r, lo, fp, lp, lp - fp + 1});
-    longest = std::max(longest, lp - fp + 1);
   }
-  int64_t chunk = min_chunk;
-  if (!drows.empty()) {
-    const int64_t budget = (int64_t)tiles_per_cu * num_cus;
-    auto count = [&](int64_t c) {
-      int64_t s = 0;
-      for (auto& d : drows) s += (d.vis + c - 1) / c;
-      return s * Hk;
-    };
-    while (chunk < longest && count(chunk) > budget) chunk *= 2;
-  }
-  plan.chunk_pages = (int32_t)chunk;
   std::stable_sort(drows.begin(), drows.end(),
                    [](const DecRow& a, const DecRow& b) { return a.vis > b.vis; });
+  std::vector<int64_t> vis(drows.size());
+  int64_t total = 0;
+  for (size_t i = 0; i < drows.size(); ++i) {
+    vis[i] = drows[i].vis;
+    total += drows[i].vis + kPieceCost;
+  }
+  int64_t cap = std::max(min_chunk, (total + W - 1) / W) + kPieceCost;
+  if (!drows.empty())
+    while (pour(vis, cap, [](size_t, int64_t, int64_t, int64_t) {}) > W) ++cap;
+  plan.worker_pages = (int32_t)std::min<int64_t>(cap, INT32_MAX);
+  // pieces per row (the same for every KV head), then slots and merges
+  std::vector<int64_t> n_pieces(drows.size(), 0);
+  pour(vis, cap, [&](size_t i, int64_t, int64_t, int64_t) { ++n_pieces[i]; });
+  std::vector<int64_t> slot0(drows.size(), -1);
   int64_t slot = 0;
-  for (auto& d : drows) {
-    const int64_t n = kv_len[d.r];
-    const int64_t nch = (d.vis + chunk - 1) / chunk;
-    const int64_t base = slot;
-    if (nch > INT16_MAX) {
-      err = fmt_row("more than 32767 key chunks in one decode row", d.r);
-      return PKV_E_INVALID;
-    }
-    const int32_t row_ref = (int32_t)plan.decode_rows.size();
+  plan.decode_rows.reserve(drows.size());
+  for (size_t i = 0; i < drows.size(); ++i) {
+    const DecRow& d = drows[i];
+    const int64_t nch = n_pieces[i];
     DecodeRowMeta rm{};
     rm.page_base = kv_indptr[d.r];
     rm.q_index = q_start[d.r];
-    rm.kv_len = (int32_t)n;
-    rm.slot0 = nch > 1 ? (int32_t)base : -1;
+    rm.kv_len = kv_len[d.r];
+    rm.slot0 = nch > 1 ? (int32_t)std::min<int64_t>(slot, INT32_MAX) : -1;
     rm.n_chunks = (int32_t)nch;
     plan.decode_rows.push_back(rm);
-    for (int64_t i = 0; i < nch; ++i) {
-      const int64_t p0 = d.fp + i * d.vis / nch, p1 = d.fp + (i + 1) * d.vis / nch;
-      const int64_t ks = std::max(d.lo, p0 * ps);
-      const int64_t ke = std::min(n, p1 * ps);
-      for (int32_t hk = 0; hk < Hk; ++hk) {
-        pkv_decode_tile t;
-        t.row = d.r;
-        t.kv_head = hk;
-        t.kv_start = (int32_t)ks;
-        t.kv_end = (int32_t)ke;
-        t.page_base = kv_indptr[d.r];
-        t.q_index = q_start[d.r];
-        t.out_slot = nch > 1 ? (int32_t)(base + hk * nch + i) : -1;
-        t.kv_len = (int32_t)n;
-        plan.decode_tiles.push_back(t);
-        plan.decode_tile_meta.push_back(
-            {row_ref, (int16_t)hk, (int16_t)i, (int32_t)ks, (int32_t)ke});
-      }
-    }
     if (nch > 1) {
+      slot0[i] = slot;
       for (int32_t hk = 0; hk < Hk; ++hk)
-        plan.merges.push_back({q_start[d.r], hk, (int32_t)(base + hk * nch), (int32_t)nch});
+        plan.merges.push_back({q_start[d.r], hk, (int32_t)(slot + hk * nch), (int32_t)nch});
       slot += Hk * nch;
       plan.max_merge_chunks = std::max(plan.max_merge_chunks, (int32_t)nch);
     }
-  }
-  if (slot > INT32_MAX) {
-    err = "too many split-KV partials";
-    return PKV_E_INVALID;
+    if (slot > INT32_MAX) {
+      err = "too many split-KV partials";
+      return PKV_E_INVALID;
+    }
   }
   plan.n_slots = (int32_t)slot;
+  // the pieces, in pour order, and each worker's piece range
+  std::vector<int64_t> chunk_of(drows.size(), 0);
+  int64_t last_worker = -1;
+  pour(vis, cap, [&](size_t i, int64_t off, int64_t take, int64_t wk) {
+    const DecRow& d = drows[i];
+    const int64_t n = kv_len[d.r];
+    const int64_t p0 = d.fp + off, p1 = p0 + take;
+    const int32_t ks = (int32_t)std::max(d.lo, p0 * ps);
+    const int32_t ke = (int32_t)std::min(n, p1 * ps);
+    const int32_t ch = (int32_t)chunk_of[i]++;
+    while (last_worker < wk) {
+      plan.decode_work.push_back((int32_t)plan.decode_pieces.size());
+      ++last_worker;
+    }
+    plan.decode_pieces.push_back({(int32_t)i, ch, ks, ke});
+    for (int32_t hk = 0; hk < Hk; ++hk) {
+      pkv_decode_tile t;
+      t.row = d.r;
+      t.kv_head = hk;
+      t.kv_start = ks;
+      t.kv_end = ke;
+      t.page_base = kv_indptr[d.r];
+      t.q_index = q_start[d.r];
+      t.out_slot = slot0[i] >= 0 ? (int32_t)(slot0[i] + hk * n_pieces[i] + ch) : -1;
+      t.kv_len = (int32_t)n;
+      plan.decode_tiles.push_back(t);
+    }
+  });
+  plan.n_workers = (int32_t)(last_worker + 1);
+  plan.decode_work.push_back((int32_t)plan.decode_pieces.size());
 
   // ---- prefill tiles ----
   make_prefill_tiles(P, pre_rows, kv_len, q_len, q_start,
@@ -456,12 +512,15 @@ pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
     plan.caps = static_caps(P, num_cus);
     const PlanData::Caps& c = plan.caps;
     if ((int64_t)plan.decode_rows.size() > c.dec_rows ||
-        (int64_t)plan.decode_tile_meta.size() > c.dec_tiles ||
+        (int64_t)plan.decode_pieces.size() > c.dec_pieces || plan.n_workers > c.dec_workers ||
         (int64_t)plan.merges.size() > c.merges || plan.n_slots > c.n_slots ||
         (int64_t)plan.prefill_tiles.size() > c.prefill_tiles) {
       err = "internal: a graph-static plan outgrew its capacities";
       return PKV_E_CAPACITY;
     }
+    // every worker of the capacity grid reads its range: the unused ones get
+    // empty ranges at the end
+    plan.decode_work.resize(c.dec_workers + 1, (int32_t)plan.decode_pieces.size());
   }
   layout_workspace(plan);
   out = std::move(plan);
@@ -471,7 +530,7 @@ pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
 void serialize_meta(const PlanData& plan, void* dst) {
   char* base = static_cast<char*>(dst);
   std::memset(base, 0, plan.ws.meta_bytes);
-  const int64_t hdr[8] = {(int64_t)plan.decode_tiles.size(), (int64_t)plan.merges.size(),
+  const int64_t hdr[8] = {(int64_t)plan.decode_pieces.size(), (int64_t)plan.merges.size(),
                           (int64_t)plan.prefill_tiles.size(), (int64_t)plan.indices.size(),
                           (int64_t)plan.slots.size(), plan.n_slots, plan.total_q, plan.batch};
   std::memcpy(base, hdr, sizeof(hdr));
@@ -482,8 +541,10 @@ void serialize_meta(const PlanData& plan, void* dst) {
       plan.dense_rows.size() * sizeof(DenseRowMeta));
   put(plan.ws.off_decode_rows, plan.decode_rows.data(),
       plan.decode_rows.size() * sizeof(DecodeRowMeta));
-  put(plan.ws.off_decode_tiles, plan.decode_tile_meta.data(),
-      plan.decode_tile_meta.size() * sizeof(DecodeTileMeta));
+  put(plan.ws.off_decode_tiles, plan.decode_pieces.data(),
+      plan.decode_pieces.size() * sizeof(DecodePieceMeta));
+  put(plan.ws.off_decode_work, plan.decode_work.data(),
+      plan.decode_work.size() * sizeof(int32_t));
   put(plan.ws.off_merges, plan.merges.data(), plan.merges.size() * sizeof(pkv_merge_entry));
   put(plan.ws.off_prefill_tiles, plan.prefill_tiles.data(),
       plan.prefill_tiles.size() * sizeof(pkv_prefill_tile));

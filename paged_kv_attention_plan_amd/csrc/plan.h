@@ -1,6 +1,7 @@
 // Host-side planner for paged-KV attention: page-table validation, work tiles,
-// split-KV chunking, workspace layout, KV write slots and the mixed-step
-// permutation.  No HIP dependency: everything here is plain C++ on the host.
+// the balanced split-KV partition of decode work, workspace layout, KV write
+// slots and the mixed-step permutation.  No HIP dependency: everything here is
+// plain C++ on the host.
 #pragma once
 
 #include <cstddef>
@@ -19,7 +20,8 @@ namespace pkv {
 struct WorkspaceLayout {
   size_t off_dense_rows = 0;      // DenseRowMeta per row of a dense plan
   size_t off_decode_rows = 0;     // DecodeRowMeta per decode row
-  size_t off_decode_tiles = 0;    // DecodeTileMeta per decode tile
+  size_t off_decode_tiles = 0;    // DecodePieceMeta per decode piece
+  size_t off_decode_work = 0;     // int32 piece range start per decode worker, plus the end
   size_t off_merges = 0;          // pkv_merge_entry per split (row, KV head)
   size_t off_prefill_tiles = 0;
   size_t off_indices = 0;
@@ -36,7 +38,8 @@ struct PlanData {
   int32_t total_q = 0;
   int32_t num_cus = 0;
   int32_t group = 1;
-  int32_t chunk_pages = 0;
+  int32_t worker_pages = 0;      // decode balance target: pages (+ overheads) per worker
+  int32_t n_workers = 0;         // decode workers of this plan (capacity if graph-static)
   int32_t n_slots = 0;
   int32_t max_merge_chunks = 0;  // largest n_chunks over merges
   int32_t n_decode_rows = 0;
@@ -44,7 +47,8 @@ struct PlanData {
   std::vector<pkv_decode_tile> decode_tiles;
   std::vector<pkv_merge_entry> merges;         // every split (row, KV head)
   std::vector<DecodeRowMeta> decode_rows;      // device form of the decode tiles
-  std::vector<DecodeTileMeta> decode_tile_meta;
+  std::vector<DecodePieceMeta> decode_pieces;  // each run by the Hk waves of a worker
+  std::vector<int32_t> decode_work;            // n_workers + 1 piece offsets
   std::vector<pkv_prefill_tile> prefill_tiles;
   std::vector<int32_t> indices;  // copy of paged_kv_indices
   std::vector<int64_t> slots;    // flat write slot per query token
@@ -52,8 +56,8 @@ struct PlanData {
   // graph-static plans: the workspace is laid out for these capacities
   bool is_static = false;
   struct Caps {
-    int64_t dec_rows = 0, dec_tiles = 0, merges = 0, n_slots = 0, prefill_tiles = 0,
-            indices = 0, tokens = 0;
+    int64_t dec_rows = 0, dec_pieces = 0, dec_workers = 0, merges = 0, n_slots = 0,
+            prefill_tiles = 0, indices = 0, tokens = 0;
   } caps;
   // dense plans
   bool dense = false;

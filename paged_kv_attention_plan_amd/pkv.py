@@ -39,7 +39,7 @@ class PlanParams(C.Structure):
                 ("head_dim", C.c_int32), ("page_size", C.c_int32), ("causal", C.c_int32),
                 ("window_left", C.c_int32), ("dtype", C.c_int32), ("max_prefill_rows", C.c_int32),
                 ("num_cus", C.c_int32), ("max_pages", C.c_int64),
-                ("decode_tiles_per_cu", C.c_int32), ("decode_min_chunk_pages", C.c_int32),
+                ("decode_waves_per_cu", C.c_int32), ("decode_min_chunk_pages", C.c_int32),
                 ("static_max_batch", C.c_int32), ("static_max_tokens", C.c_int32),
                 ("static_max_page_entries", C.c_int64)]
 
@@ -142,7 +142,7 @@ def version() -> str:
 
 def plan_params(kind="decode", *, num_qo_heads, num_kv_heads, head_dim, page_size, max_pages,
                 causal=True, window_left=-1, max_prefill_rows=0, num_cus=0,
-                decode_tiles_per_cu=0, decode_min_chunk_pages=0, static_max_batch=0,
+                decode_waves_per_cu=0, decode_min_chunk_pages=0, static_max_batch=0,
                 static_max_tokens=0, static_max_page_entries=0) -> PlanParams:
     p = PlanParams()
     _lib.pkv_plan_params_init(C.byref(p))
@@ -150,7 +150,7 @@ def plan_params(kind="decode", *, num_qo_heads, num_kv_heads, head_dim, page_siz
     p.num_qo_heads, p.num_kv_heads, p.head_dim, p.page_size = num_qo_heads, num_kv_heads, head_dim, page_size
     p.causal, p.window_left, p.dtype = int(bool(causal)), int(window_left), DTYPE_BF16
     p.max_prefill_rows, p.num_cus, p.max_pages = int(max_prefill_rows), int(num_cus), int(max_pages)
-    p.decode_tiles_per_cu, p.decode_min_chunk_pages = int(decode_tiles_per_cu), int(decode_min_chunk_pages)
+    p.decode_waves_per_cu, p.decode_min_chunk_pages = int(decode_waves_per_cu), int(decode_min_chunk_pages)
     p.static_max_batch, p.static_max_tokens = int(static_max_batch), int(static_max_tokens)
     p.static_max_page_entries = int(static_max_page_entries)
     return p
@@ -205,12 +205,12 @@ class Plan:
         return buf
 
     def info(self) -> dict:
-        v = (C.c_int64 * 16)()
+        v = (C.c_int64 * 18)()
         _check(_lib.pkv_plan_info(self._h, v))
-        keys = ["total_q", "batch", "decode_rows", "prompt_rows", "chunk_pages", "partial_slots",
+        keys = ["total_q", "batch", "decode_rows", "prompt_rows", "worker_pages", "partial_slots",
                 "meta_bytes", "workspace_bytes", "num_cus", "total_k", "off_dense_rows",
-                "off_decode_rows", "off_decode_tiles", "off_merges", "off_prefill_tiles",
-                "off_indices"]
+                "off_decode_rows", "off_decode_pieces", "off_merges", "off_prefill_tiles",
+                "off_indices", "off_decode_work", "decode_workers"]
         return {k: int(v[i]) for i, k in enumerate(keys)}
 
 

@@ -41,10 +41,11 @@ def _layout(w):
 
 
 DECODE_CASES = [
-    dict(seed=40, page_size=16, head_dim=64, window_left=-1, num_cus=1, tpc=4, mcp=1),
-    dict(seed=41, page_size=1, head_dim=128, window_left=-1, num_cus=2, tpc=8, mcp=2),
-    dict(seed=42, page_size=4, head_dim=64, window_left=17, num_cus=1, tpc=2, mcp=1),
-    dict(seed=43, page_size=32, head_dim=128, window_left=0, num_cus=256, tpc=0, mcp=0),
+    dict(seed=40, page_size=16, head_dim=64, window_left=-1, num_cus=1, wpc=4, mcp=1),
+    dict(seed=41, page_size=1, head_dim=128, window_left=-1, num_cus=2, wpc=8, mcp=2),
+    dict(seed=42, page_size=4, head_dim=64, window_left=17, num_cus=1, wpc=2, mcp=1),
+    dict(seed=43, page_size=32, head_dim=128, window_left=0, num_cus=256, wpc=0, mcp=0),
+    dict(seed=44, page_size=16, head_dim=128, window_left=-1, num_cus=3, wpc=0, mcp=1),
 ]
 
 
@@ -52,20 +53,25 @@ DECODE_CASES = [
 def test_decode_plan_matches_policy(c):
     w = synth.random_case(c["seed"], kind="decode", batch=7, head_dim=c["head_dim"],
                           page_size=c["page_size"], max_kv=300, window_left=c["window_left"])
-    plan = pkv.plan_create(_params(w, "decode", num_cus=c["num_cus"], decode_tiles_per_cu=c["tpc"],
+    plan = pkv.plan_create(_params(w, "decode", num_cus=c["num_cus"], decode_waves_per_cu=c["wpc"],
                                    decode_min_chunk_pages=c["mcp"]),
                            None, w.kv_indptr, w.kv_indices, w.last_page_len)
     lay = _layout(w)
     rows = list(range(w.batch))
-    tiles, merges, chunk, n_slots = oracle.decode_policy(
+    tiles, merges, cap, n_slots, work = oracle.decode_policy(
         lay, rows, page_size=w.page_size, num_kv_heads=w.num_kv_heads, window_left=w.window_left,
         num_cus=c["num_cus"], qo_indptr=w.qo_indptr, kv_indptr=w.kv_indptr,
-        tiles_per_cu=c["tpc"] or 32, min_chunk_pages=c["mcp"] or 8)
+        group=w.num_qo_heads // w.num_kv_heads, waves_per_cu=c["wpc"],
+        min_chunk_pages=c["mcp"] or 8)
     got = [tuple(int(x) for x in t) for t in plan.decode_tiles()]
     assert got == tiles
     assert [tuple(int(x) for x in m) for m in plan.merges()] == merges
     info = plan.info()
-    assert info["chunk_pages"] == chunk and info["partial_slots"] == n_slots
+    assert info["worker_pages"] == cap and info["partial_slots"] == n_slots
+    assert info["decode_workers"] == len(work) - 1
+    img = plan.metadata()
+    off = info["off_decode_work"]
+    assert list(img[off:off + 4 * len(work)].view(np.int32)) == work
     oracle.check_decode_cover(got, merges, lay, rows, num_kv_heads=w.num_kv_heads,
                               window_left=w.window_left, n_slots=n_slots)
     slots = oracle.write_slots(w.page_size, w.kv_indptr, w.kv_indices, w.last_page_len)
@@ -109,9 +115,10 @@ def test_mixed_plan_rows_and_permutation():
     assert sorted({int(t["row"]) for t in plan.decode_tiles()}) == list(dec)
     assert sorted({int(t["row"]) for t in plan.prefill_tiles()}) == list(pre)
     lay = _layout(w)
-    tiles, merges, chunk, n_slots = oracle.decode_policy(
+    tiles, merges, cap, n_slots, work = oracle.decode_policy(
         lay, list(dec), page_size=w.page_size, num_kv_heads=w.num_kv_heads,
-        window_left=w.window_left, num_cus=4, qo_indptr=w.qo_indptr, kv_indptr=w.kv_indptr)
+        window_left=w.window_left, num_cus=4, qo_indptr=w.qo_indptr, kv_indptr=w.kv_indptr,
+        group=w.num_qo_heads // w.num_kv_heads)
     assert [tuple(int(x) for x in t) for t in plan.decode_tiles()] == tiles
     want = oracle.prefill_policy(lay, list(pre), num_qo_heads=w.num_qo_heads,
                                  num_kv_heads=w.num_kv_heads, causal=True,

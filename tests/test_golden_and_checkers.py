@@ -36,9 +36,10 @@ def test_decode_policy_passes_cover_check(window_left):
                           window_left=window_left)
     lay = _layout(w)
     rows = list(range(w.batch))
-    tiles, merges, chunk, n_slots = oracle.decode_policy(
+    tiles, merges, cap, n_slots, work = oracle.decode_policy(
         lay, rows, page_size=4, num_kv_heads=2, window_left=window_left, num_cus=2,
-        qo_indptr=w.qo_indptr, kv_indptr=w.kv_indptr, tiles_per_cu=16, min_chunk_pages=2)
+        qo_indptr=w.qo_indptr, kv_indptr=w.kv_indptr, group=w.num_qo_heads // 2,
+        waves_per_cu=8, min_chunk_pages=2)
     oracle.check_decode_cover(tiles, merges, lay, rows, num_kv_heads=2, window_left=window_left,
                               n_slots=n_slots)
     if window_left in (-1, 40):

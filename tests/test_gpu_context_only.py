@@ -67,7 +67,7 @@ def test_context_only_decode(pkv, gpu, seed, split):
     w = synth.random_case(seed, kind="decode", batch=9, num_qo_heads=32, num_kv_heads=8,
                           head_dim=128, page_size=16, max_kv=900, stale="nan", device=gpu)
     v = _views(pkv, w, seed, one_query=True)
-    kw = dict(num_cus=64, decode_tiles_per_cu=16, decode_min_chunk_pages=1) if split else {}
+    kw = dict(num_cus=64, decode_waves_per_cu=16, decode_min_chunk_pages=1) if split else {}
     out, lse, plan, _ = gpu_run(pkv, v, **kw)
     if split:
         assert len(plan.merges()) > 0

@@ -62,7 +62,7 @@ def test_captured_step_replays_with_new_plans(pkv, gpu, kind, seeds):
                              static_max_batch=B_cap, static_max_tokens=T_cap,
                              static_max_page_entries=POOL,
                              # small tiles budget so that rows split and merges run
-                             num_cus=32, decode_tiles_per_cu=4, decode_min_chunk_pages=1)
+                             num_cus=32, decode_waves_per_cu=4, decode_min_chunk_pages=1)
     qo = lambda w: None if kind == "decode" else w.qo_indptr
     plan = pkv.plan_create(params, qo(w0), w0.kv_indptr, w0.kv_indices, w0.last_page_len)
     ws = torch.empty(plan.ws_bytes, dtype=torch.uint8, device=gpu)

@@ -67,7 +67,7 @@ def test_decode_small(pkv, gpu, case):
                           head_dim=D, page_size=ps, max_kv=700, window_left=wl, stale=stale,
                           device=gpu)
     # a large tile budget with 1-page chunks makes the planner cut rows into chunks
-    kw = dict(num_cus=64, decode_tiles_per_cu=16, decode_min_chunk_pages=1) if split else {}
+    kw = dict(num_cus=64, decode_waves_per_cu=16, decode_min_chunk_pages=1) if split else {}
     out, lse, plan, _ = gpu_run(pkv, w, **kw)
     if split:
         assert len(plan.merges()) > 0
@@ -166,7 +166,7 @@ def test_repeat_runs_are_deterministic(pkv, gpu):
     say("case repeat determinism (split decode)")
     w = synth.random_case(330, kind="decode", batch=9, num_qo_heads=32, num_kv_heads=8,
                           head_dim=128, page_size=16, max_kv=900, device=gpu)
-    kw = dict(num_cus=64, decode_tiles_per_cu=16, decode_min_chunk_pages=1)
+    kw = dict(num_cus=64, decode_waves_per_cu=16, decode_min_chunk_pages=1)
     o1, l1, p1, _ = gpu_run(pkv, w, **kw)
     o2, l2, _, _ = gpu_run(pkv, w, **kw)
     assert len(p1.merges()) > 0

@@ -15,7 +15,7 @@ from gpu_common import compare, params_for, say
 
 pytestmark = pytest.mark.gpu
 
-SPLIT = dict(num_cus=64, decode_tiles_per_cu=16, decode_min_chunk_pages=1)
+SPLIT = dict(num_cus=64, decode_waves_per_cu=16, decode_min_chunk_pages=1)
 
 
 @pytest.fixture(scope="module")

@@ -3,11 +3,12 @@ copies into the workspace), decoded on the CPU the way the kernels decode it.
 
 For every workload shape (full-size lengths, forced split-KV, graph-static and
 dense plans) the image must agree with the public tile lists, and every index
-a kernel derives from it must stay inside its buffer: a decode tile's row
-record gives its page base, query and partial slot; its keys lie in the row's
-pages; merges address existing partial slots; prefill tiles, page indices and
-write slots are the planned ones; regions do not overlap and fit the
-workspace.  No GPU is involved.
+a kernel derives from it must stay inside its buffer: the worker table gives
+every decode wave a range of pieces inside the piece list; a piece's row
+record gives its page base, query and partial slot for each KV head; its keys
+lie in the row's pages; merges address existing partial slots; prefill tiles,
+page indices and write slots are the planned ones; regions do not overlap and
+fit the workspace.  No GPU is involved.
 """
 import numpy as np
 import pytest
@@ -17,7 +18,7 @@ import synth
 pkv = pytest.importorskip("paged_kv_attention_plan_amd.pkv",
                           reason="libpkv.so not built (python -m paged_kv_attention_plan_amd.build)")
 
-DTILE = np.dtype([("row", "<i4"), ("kv_head", "<i2"), ("chunk", "<i2"), ("ks", "<i4"), ("ke", "<i4")])
+PIECE = np.dtype([("row", "<i4"), ("chunk", "<i4"), ("ks", "<i4"), ("ke", "<i4")])
 DROW = np.dtype([("page_base", "<i4"), ("q_index", "<i4"), ("kv_len", "<i4"), ("slot0", "<i4"),
                  ("n_chunks", "<i4"), ("pad", "<i4", (3,))])
 NROW = np.dtype([("cu_k", "<i4"), ("cu_q", "<i4"), ("prefix", "<i4"), ("fresh", "<i4"),
@@ -36,25 +37,38 @@ def _check(plan, kind, kv_indptr, kv_indices, last_page_len, qo_indptr, hk, g, d
     hdr = img[:64].view(np.int64)
     n_dt, n_m, n_pt, n_idx, n_sl, n_slots, T, B = (int(x) for x in hdr)
     pub = plan.decode_tiles()
-    assert n_dt == len(pub) and n_m == len(plan.merges()) and n_pt == len(plan.prefill_tiles())
+    assert n_m == len(plan.merges()) and n_pt == len(plan.prefill_tiles())
     assert n_idx == len(kv_indices) and T == info["total_q"] and B == info["batch"]
     assert n_slots == info["partial_slots"] and n_sl == len(plan.write_slots())
     # regions in order, each inside the metadata image
-    offs = [info["off_dense_rows"], info["off_decode_rows"], info["off_decode_tiles"],
-            info["off_merges"], info["off_prefill_tiles"], info["off_indices"]]
+    offs = [info["off_dense_rows"], info["off_decode_rows"], info["off_decode_pieces"],
+            info["off_decode_work"], info["off_merges"], info["off_prefill_tiles"],
+            info["off_indices"]]
     assert offs[0] == 256 and offs == sorted(offs) and offs[-1] <= info["meta_bytes"]
-    # decode tiles through the row table, as the decode kernel reads them
+    # the worker table, as the decode kernel's waves read it: worker w (Hk waves)
+    # runs pieces [work[w], work[w + 1]); every piece belongs to one worker
+    n_w = info["decode_workers"]
+    assert (n_w + 1) * 4 <= offs[4] - offs[3]
+    work = img[offs[3]:offs[3] + 4 * (n_w + 1)].view(np.int32)
+    if n_dt:
+        assert work[0] == 0 and work[-1] == n_dt and np.all(np.diff(work) >= 0)
+    else:
+        assert np.all(work == 0)
+    # decode pieces through the row table, as the decode kernel reads them
     n_rows = (offs[2] - offs[1]) // DROW.itemsize
     rows = img[offs[1]:offs[1] + n_rows * DROW.itemsize].view(DROW)
-    tiles = img[offs[2]:offs[2] + n_dt * DTILE.itemsize].view(DTILE)
-    assert n_dt * DTILE.itemsize <= offs[3] - offs[2]
-    for t, (tm, pt) in enumerate(zip(tiles, pub)):
+    pieces = img[offs[2]:offs[2] + n_dt * PIECE.itemsize].view(PIECE)
+    assert n_dt * PIECE.itemsize <= offs[3] - offs[2]
+    assert len(pub) == n_dt * hk
+    for t, pt in enumerate(pub):
+        tm = pieces[t // hk]
+        assert pt["kv_head"] == t % hk
         assert 0 <= tm["row"] < n_rows
         r = rows[tm["row"]]
         assert (r["page_base"], r["q_index"], r["kv_len"]) == (pt["page_base"], pt["q_index"], pt["kv_len"])
-        assert (tm["kv_head"], tm["ks"], tm["ke"]) == (pt["kv_head"], pt["kv_start"], pt["kv_end"])
-        assert 0 <= tm["chunk"] < r["n_chunks"] and 0 <= tm["kv_head"] < hk
-        slot = r["slot0"] + tm["kv_head"] * r["n_chunks"] + tm["chunk"] if r["slot0"] >= 0 else -1
+        assert (tm["ks"], tm["ke"]) == (pt["kv_start"], pt["kv_end"])
+        assert 0 <= tm["chunk"] < r["n_chunks"]
+        slot = r["slot0"] + pt["kv_head"] * r["n_chunks"] + tm["chunk"] if r["slot0"] >= 0 else -1
         assert slot == pt["out_slot"] and slot < n_slots
         assert 0 <= r["q_index"] < T
         assert 0 <= tm["ks"] < tm["ke"] <= r["kv_len"]
@@ -62,19 +76,19 @@ def _check(plan, kind, kv_indptr, kv_indices, last_page_len, qo_indptr, hk, g, d
         first, last = r["page_base"] + tm["ks"] // ps, r["page_base"] + (tm["ke"] - 1) // ps
         assert kv_indptr[row] <= first and last < kv_indptr[row + 1]
     # merges, as the merge kernel reads them
-    mer = img[offs[3]:offs[3] + n_m * 16].view(np.int32).reshape(-1, 4)
-    assert n_m * 16 <= offs[4] - offs[3]
+    mer = img[offs[4]:offs[4] + n_m * 16].view(np.int32).reshape(-1, 4)
+    assert n_m * 16 <= offs[5] - offs[4]
     assert np.array_equal(mer, plan.merges().view(np.int32).reshape(-1, 4))
     for q_index, head, base, n in mer:
         assert 0 <= q_index < T and 0 <= head < hk and 0 <= base and base + n <= n_slots and n >= 2
     # prefill tiles, page indices and write slots are the planned ones
-    pre = img[offs[4]:offs[4] + n_pt * 48]
-    assert n_pt * 48 <= offs[5] - offs[4]
+    pre = img[offs[5]:offs[5] + n_pt * 48]
+    assert n_pt * 48 <= offs[6] - offs[5]
     assert np.array_equal(pre, plan.prefill_tiles().view(np.uint8).reshape(-1))
-    assert np.array_equal(img[offs[5]:offs[5] + 4 * n_idx].view(np.int32), kv_indices)
+    assert np.array_equal(img[offs[6]:offs[6] + 4 * n_idx].view(np.int32), kv_indices)
     slot_cap = static_tokens if static_tokens is not None else n_sl
     off_slots = info["meta_bytes"] - _a256(8 * slot_cap)
-    assert off_slots >= offs[5] + 4 * n_idx
+    assert off_slots >= offs[6] + 4 * n_idx
     assert np.array_equal(img[off_slots:off_slots + 8 * n_sl].view(np.int64), plan.write_slots())
     # partials fit the workspace
     need = _a256(n_slots * g * d * 4) + _a256(n_slots * g * 4)
@@ -127,7 +141,7 @@ def test_forced_split_images(seed, kind, ps, wl, static):
         w = synth.from_lengths("m", "mixed", w.kv_len, ql, num_qo_heads=16, num_kv_heads=4,
                                head_dim=64, page_size=ps, window_left=wl, seed=seed,
                                max_prefill_rows=3)
-    _run(w, kind, static=static, num_cus=16, decode_tiles_per_cu=8, decode_min_chunk_pages=1)
+    _run(w, kind, static=static, num_cus=16, decode_waves_per_cu=8, decode_min_chunk_pages=1)
 
 
 def test_dense_rows_image():
