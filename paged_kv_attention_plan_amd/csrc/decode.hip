@@ -17,8 +17,11 @@
 // group's G query heads (bf16 dot2), then a DPP allreduce over its LPK lanes.
 // Softmax: the KPL lane groups of a wave each keep their own running max, sum
 // and output accumulator (fp32, in registers) over the keys they see; the
-// groups are combined once, at the end of the piece, by log-sum-exp.  Only
-// blocks that cross a piece's first or last key mask keys.
+// groups are combined once, at the end of the piece, by log-sum-exp.  The
+// running max moves only when a block exceeds it by more than 2^8, and P.V
+// takes two keys per v_dot2_f32_bf16 with P rounded to bf16, so the vector ALU
+// work per byte stays well below what the stream leaves room for.  Only blocks
+// that cross a piece's first or last key mask keys.
 //
 // Memory traffic is one read of every visible K and V byte: the kernel is
 // bound by HBM bandwidth.
@@ -140,6 +143,7 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int piece, int
     }
   };
 
+  const float sc = a.scale_log2;  // log2(e) / sqrt(D): scores in log2 units
   auto compute_blk = [&](const uint4 (&kk)[U], const uint4 (&vv)[U], int b, auto edge_c) {
     constexpr bool kEdge = decltype(edge_c)::value;
     const int kb = kb0 + b * KB;
@@ -152,7 +156,7 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int piece, int
         acc = dot2_bf16(qw[h][1], kk[u].y, acc);
         acc = dot2_bf16(qw[h][2], kk[u].z, acc);
         acc = dot2_bf16(qw[h][3], kk[u].w, acc);
-        s[u][h] = group_sum<LPK>(acc) * a.scale_log2;
+        s[u][h] = group_sum<LPK>(acc);  // unscaled: the scale is folded into exp2 below
       }
     }
     bool ok[U];
@@ -165,37 +169,59 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int piece, int
         for (int h = 0; h < G; ++h) s[u][h] = ok[u] ? s[u][h] : -INFINITY;
       }
     }
-    // New running max per head; rescale what was accumulated so far.
+    // Running max per head, in scaled (log2) units, moved lazily: only when a
+    // block's maximum exceeds it by more than 8 (probabilities then stay below
+    // 2^8), and then for every head of the wave at once behind a uniform branch.
+    float mxs[G];
+    bool grow = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float mx = s[0][h];
 #pragma unroll
       for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][h]);
-      const float mn = fmaxf(m[h], mx);
-      const float alpha = fast_exp2(m[h] - mn);
-      m[h] = mn;
-      l[h] *= alpha;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+      mxs[h] = mx * sc;
+      grow = grow || mxs[h] > m[h] + 8.f;
     }
-    // One key row at a time: widen its V once, use it for every head.
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float vf[8];
-      vf[0] = bf16_lo(vv[u].x); vf[1] = bf16_hi(vv[u].x);
-      vf[2] = bf16_lo(vv[u].y); vf[3] = bf16_hi(vv[u].y);
-      vf[4] = bf16_lo(vv[u].z); vf[5] = bf16_hi(vv[u].z);
-      vf[6] = bf16_lo(vv[u].w); vf[7] = bf16_hi(vv[u].w);
-      if constexpr (kEdge) {
+      for (int h = 0; h < G; ++h) {
+        const float mn = fmaxf(m[h], mxs[h]);
+        const float alpha = fast_exp2(m[h] - mn);
+        m[h] = mn;
+        l[h] *= alpha;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vf[e] = ok[u] ? vf[e] : 0.f;  // stale slots may hold NaN
+        for (int e = 0; e < 8; ++e) o[h][e] *= alpha;
+      }
+    }
+    // Two key rows at a time: their V, interleaved per dimension into bf16
+    // pairs, and each head's two probabilities rounded to a bf16 pair give
+    // o += p0*v0 + p1*v1 in one v_dot2_f32_bf16 per dimension.  The sum l
+    // takes the fp32 probabilities.
+#pragma unroll
+    for (int u = 0; u < U; u += 2) {
+      uint32_t w0[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+      uint32_t w1[4] = {vv[u + 1].x, vv[u + 1].y, vv[u + 1].z, vv[u + 1].w};
+      if constexpr (kEdge) {  // stale slots may hold NaN
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          w0[i] = ok[u] ? w0[i] : 0u;
+          w1[i] = ok[u + 1] ? w1[i] : 0u;
+        }
+      }
+      uint32_t vp[8];  // vp[e] = (v0[e], v1[e]) as a bf16 pair
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vp[2 * i] = __builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u);
+        vp[2 * i + 1] = __builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u);
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float p = fast_exp2(s[u][h] - m[h]);
-        l[h] += p;
+        const float p0 = fast_exp2(fmaf(s[u][h], sc, -m[h]));
+        const float p1 = fast_exp2(fmaf(s[u + 1][h], sc, -m[h]));
+        l[h] += p0 + p1;
+        const uint32_t pp = cvt_bf16x2(p0, p1);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vf[e], o[h][e]);
+        for (int e = 0; e < 8; ++e) o[h][e] = dot2_bf16(pp, vp[e], o[h][e]);
       }
     }
   };
