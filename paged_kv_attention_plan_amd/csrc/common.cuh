@@ -45,6 +45,33 @@ constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowRor4 = 0x124;      // row_ror:4
+constexpr int kDppRowRor8 = 0x128;      // row_ror:8 (lane i <-> lane i ^ 8 within the row)
+
+// Lane SRC (0..15) of each row of 16 lanes, to every lane of that row
+// (DPP row_newbcast).
+template <int SRC>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
+  static_assert(SRC >= 0 && SRC < 16, "row lane");
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + SRC, 0xf, 0xf, false);
+}
+// The same with the lane given at run time: after unrolling it is a constant,
+// and the switch folds to one move.
+__device__ __forceinline__ uint32_t bcast16u(uint32_t x, int src) {
+  switch (src) {
+    case 0: return row_bcast<0>(x);    case 1: return row_bcast<1>(x);
+    case 2: return row_bcast<2>(x);    case 3: return row_bcast<3>(x);
+    case 4: return row_bcast<4>(x);    case 5: return row_bcast<5>(x);
+    case 6: return row_bcast<6>(x);    case 7: return row_bcast<7>(x);
+    case 8: return row_bcast<8>(x);    case 9: return row_bcast<9>(x);
+    case 10: return row_bcast<10>(x);  case 11: return row_bcast<11>(x);
+    case 12: return row_bcast<12>(x);  case 13: return row_bcast<13>(x);
+    case 14: return row_bcast<14>(x);  default: return row_bcast<15>(x);
+  }
+}
+__device__ __forceinline__ float bcast16(float x, int src) {
+  return __builtin_bit_cast(float, bcast16u(__builtin_bit_cast(uint32_t, x), src));
+}
 
 // Sum over groups of N consecutive lanes (N = 4, 8 or 16); every lane of a
 // group receives the group's sum.

@@ -14,7 +14,11 @@
 // are streamed once, so they are loaded non-temporal.
 //
 // Scores: each lane forms the partial dot product of its 8 dimensions with the
-// group's G query heads (bf16 dot2), then a DPP allreduce over its LPK lanes.
+// group's G query heads (bf16 dot2).  With D = 128 and G of 4 or 8 a block
+// holds 16 (key, head) pairs per 16-lane key row; a DPP reduce-scatter leaves
+// one whole score per lane, so each exponential is taken once, and the
+// probabilities return to the lanes by row broadcasts.  Other shapes use a DPP
+// allreduce over the LPK lanes of a key.
 // Softmax: the KPL lane groups of a wave each keep their own running max, sum
 // and output accumulator (fp32, in registers) over the keys they see; the
 // groups are combined once, at the end of the piece, by log-sum-exp.  The
@@ -98,6 +102,12 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int piece, int
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
   }
+  // Scattered softmax (D 128, 16 (key, head) pairs per block): lane li of a key
+  // row's 16 lanes owns pair li, i.e. head li % G of key row kt_u(li); it keeps
+  // its head's running max and its own share of the sum.
+  constexpr bool kScatter = LPK == 16 && U * G == 16;
+  const int li = lane & 15;
+  float m_own = -1e30f, lsum = 0.f;
 
   // Key blocks of KB keys: block b starts at kb0 + b*KB; the last one holds key ke-1.
   const int kb0 = ks & ~(KB - 1);
@@ -144,9 +154,102 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int piece, int
   };
 
   const float sc = a.scale_log2;  // log2(e) / sqrt(D): scores in log2 units
+  // Pair q of a block: key row u and head h with q = h + G * pair_u(u), where
+  // for G = 4 the key rows 0, 1, 2, 3 sit at 0, 8, 4, 12 (and for G = 8 rows 0,
+  // 1 at 0, 8), so the two keys of a P.V pair are 8 lanes apart (row_ror:8).
+  auto pair_of = [](int u) { return G == 4 ? ((u & 1) << 3) | ((u >> 1) << 2) : u << 3; };
+  auto scatter_blk = [&](const uint4 (&kk)[U], const uint4 (&vv)[U], int kb, auto edge_c) {
+    constexpr bool kEdge = decltype(edge_c)::value;
+    // Partial dot products of this lane's 8 dimensions, all 16 pairs.
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float acc = dot2_bf16(qw[h][0], kk[u].x, 0.f);
+        acc = dot2_bf16(qw[h][1], kk[u].y, acc);
+        acc = dot2_bf16(qw[h][2], kk[u].z, acc);
+        acc = dot2_bf16(qw[h][3], kk[u].w, acc);
+        v[pair_of(u) + h] = acc;
+      }
+    }
+    // Reduce-scatter over the 16 lanes: each step halves the values a lane
+    // holds; a lane keeps the half its lane bit selects, sends the other half to
+    // the partner that differs in that bit and adds what it receives.  After
+    // the four steps lane li holds the full score of pair li.
+    const bool b3 = (li & 8) != 0, b2 = (li & 4) != 0, b1 = (li & 2) != 0, b0 = (li & 1) != 0;
+    float w8[8], w4[4], w2[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      w8[k] = (b3 ? v[k + 8] : v[k]) + dpp<kDppRowRor8>(b3 ? v[k] : v[k + 8]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w4[k] = (b2 ? w8[k + 4] : w8[k]) + dpp<kDppRowHalfMirror>(b2 ? w8[k] : w8[k + 4]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      w2[k] = (b1 ? w4[k + 2] : w4[k]) + dpp<kDppQuadXor2>(b1 ? w4[k] : w4[k + 2]);
+    float sv = (b0 ? w2[1] : w2[0]) + dpp<kDppQuadXor1>(b0 ? w2[0] : w2[1]);
+    if constexpr (kEdge) {
+      const int ul = G == 4 ? ((li >> 3) & 1) | (((li >> 2) & 1) << 1) : li >> 3;
+      const int j = kb + ul * KPL + lk;
+      sv = (j >= ks && j < ke) ? sv : -INFINITY;
+    }
+    // The block's maximum of this lane's head (its lanes are li mod G apart).
+    float mx = sv;
+    if constexpr (G == 4) mx = fmaxf(mx, dpp<kDppRowRor4>(mx));
+    mx = fmaxf(mx, dpp<kDppRowRor8>(mx));
+    const float mxs = mx * sc;
+    if (__builtin_amdgcn_ballot_w64(mxs > m_own + 8.f) != 0) {
+      const float mn = fmaxf(m_own, mxs);
+      const float alpha = fast_exp2(m_own - mn);
+      m_own = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {  // lane h holds head h
+        const float ah = bcast16(alpha, h);
+        m[h] = bcast16(m_own, h);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] *= ah;
+      }
+    }
+    const float p = fast_exp2(fmaf(sv, sc, -m_own));
+    lsum += p;
+    // (p of key row u, p of key row u + 1) of one head, on the lanes of row u.
+    const uint32_t pk = cvt_bf16x2(p, dpp<kDppRowRor8>(p));
+#pragma unroll
+    for (int u = 0; u < U; u += 2) {
+      uint32_t w0[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+      uint32_t w1[4] = {vv[u + 1].x, vv[u + 1].y, vv[u + 1].z, vv[u + 1].w};
+      if constexpr (kEdge) {  // stale slots may hold NaN
+        const bool ok0 = kb + u * KPL + lk >= ks && kb + u * KPL + lk < ke;
+        const bool ok1 = kb + (u + 1) * KPL + lk >= ks && kb + (u + 1) * KPL + lk < ke;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          w0[i] = ok0 ? w0[i] : 0u;
+          w1[i] = ok1 ? w1[i] : 0u;
+        }
+      }
+      uint32_t vp[8];  // vp[e] = (v0[e], v1[e]) as a bf16 pair
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vp[2 * i] = __builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u);
+        vp[2 * i + 1] = __builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const uint32_t pp = bcast16u(pk, pair_of(u) + h);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] = dot2_bf16(pp, vp[e], o[h][e]);
+      }
+    }
+  };
   auto compute_blk = [&](const uint4 (&kk)[U], const uint4 (&vv)[U], int b, auto edge_c) {
     constexpr bool kEdge = decltype(edge_c)::value;
     const int kb = kb0 + b * KB;
+    if constexpr (kScatter) {
+      scatter_blk(kk, vv, kb, edge_c);
+      return;
+    } else {
     float s[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -224,6 +327,7 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int piece, int
         for (int e = 0; e < 8; ++e) o[h][e] = dot2_bf16(pp, vp[e], o[h][e]);
       }
     }
+    }
   };
   // A block that crosses the piece's first or last key masks per key; the
   // others (all but at most two per piece) skip the masks.  Uniform branch.
@@ -258,6 +362,13 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int piece, int
   }
   if (b < nb) compute(ka, va, b);  // odd block count: the last block is in A
 
+  if constexpr (kScatter) {  // each head's sum from its lanes' shares
+    float t = lsum;
+    if constexpr (G == 4) t += dpp<kDppRowRor4>(t);
+    t += dpp<kDppRowRor8>(t);
+#pragma unroll
+    for (int h = 0; h < G; ++h) l[h] = bcast16(t, h);
+  }
   // Combine the KPL lane groups (lanes that differ in bits >= log2(LPK)).
 #pragma unroll
   for (int h = 0; h < G; ++h) {
