@@ -38,8 +38,8 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 // DPP lane moves inside a row of 16 lanes.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                               0xf, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
+                                                            0xf, 0xf, true));
 }
 constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
@@ -53,7 +53,7 @@ constexpr int kDppRowRor8 = 0x128;      // row_ror:8 (lane i <-> lane i ^ 8 with
 template <int SRC>
 __device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
   static_assert(SRC >= 0 && SRC < 16, "row lane");
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + SRC, 0xf, 0xf, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x150 + SRC, 0xf, 0xf, true);
 }
 // The same with the lane given at run time: after unrolling it is a constant,
 // and the switch folds to one move.

@@ -87,13 +87,6 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int piece, int
       qw[h][0] = v.x; qw[h][1] = v.y; qw[h][2] = v.z; qw[h][3] = v.w;
     }
   }
-  // Let q land before the key loop starts, so every path into the loop has the
-  // same loads in flight (otherwise the loop head waits for everything): an
-  // empty asm that reads the q registers makes the compiler wait for them here.
-#pragma unroll
-  for (int h = 0; h < G; ++h) asm volatile("" ::"v"(qw[h][0]), "v"(qw[h][1]), "v"(qw[h][2]), "v"(qw[h][3]));
-  __builtin_amdgcn_sched_barrier(0);
-
   float m[G], l[G], o[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -348,6 +341,14 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, int piece, int
   // barriers keep compute from being hoisted above the loads.
   uint4 ka[U], va[U], kbuf[U], vbuf[U];
   issue(0, ONE_PAGE_PER_ITER ? page_of(0) : 0, ka, va);
+  // Let q land before the key loop starts, so every path into the loop has the
+  // same loads in flight (otherwise the loop head waits for everything): an
+  // empty asm that reads the q registers makes the compiler wait for them here,
+  // behind the first block's loads, which stay in flight.
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int h = 0; h < G; ++h) asm volatile("" ::"v"(qw[h][0]), "v"(qw[h][1]), "v"(qw[h][2]), "v"(qw[h][3]));
+  __builtin_amdgcn_sched_barrier(0);
   int pid = ONE_PAGE_PER_ITER ? page_of(1) : 0;
   int b = 0;
   for (; b + 1 < nb; b += 2) {
