@@ -81,6 +81,40 @@ def test_decode_plan_matches_policy(c):
     assert info["workspace_bytes"] >= info["meta_bytes"] + n_slots * g * (w.head_dim + 1) * 4
 
 
+@pytest.mark.parametrize("seed,hq,hk,num_cus,wpc", [(50, 32, 8, 256, 0), (51, 64, 8, 256, 0),
+                                                   (52, 12, 3, 17, 4), (53, 8, 8, 64, 16)])
+def test_decode_workers_are_balanced(seed, hq, hk, num_cus, wpc):
+    """Every decode worker's share (its pages plus 2 per piece) lies within one
+    piece cost and one page of the capacity, except the last worker's; no more
+    workers than num_cus * waves_per_cu / Hk; each worker holds at most one
+    piece of a row."""
+    rng = np.random.default_rng(seed)
+    kv = rng.integers(1, 5000, size=int(rng.integers(20, 200)))
+    w = synth.from_lengths(f"bal{seed}", "decode", kv, np.ones_like(kv), num_qo_heads=hq,
+                           num_kv_heads=hk, head_dim=128, page_size=16, seed=seed,
+                           layout_only=True)
+    plan = pkv.plan_create(_params(w, "decode", num_cus=num_cus, decode_waves_per_cu=wpc),
+                           None, w.kv_indptr, w.kv_indices, w.last_page_len)
+    info = plan.info()
+    g = hq // hk
+    W = max(1, num_cus * (wpc or (16 if g == 8 else 4)) // hk)
+    n_w, cap = info["decode_workers"], info["worker_pages"]
+    assert 1 <= n_w <= W
+    img = plan.metadata()
+    work = img[info["off_decode_work"]:info["off_decode_work"] + 4 * (n_w + 1)].view(np.int32)
+    tiles = plan.decode_tiles()
+    pages = [-(-(int(t["kv_end"]) - int(t["kv_start"] // 16 * 16)) // 16) for t in tiles[::hk]]
+    rows = [int(t["row"]) for t in tiles[::hk]]
+    loads = []
+    for k in range(n_w):
+        ps = range(work[k], work[k + 1])
+        assert len({rows[p] for p in ps}) == len(ps)
+        loads.append(sum(pages[p] + 2 for p in ps))
+    assert max(loads) <= cap
+    assert min(loads[:-1], default=cap) >= cap - 2 - 1
+    assert sum(pages) == sum(-(-int(n) // 16) for n in kv)
+
+
 @pytest.mark.parametrize("causal,window_left,hq,hk,ps", [
     (True, -1, 8, 2, 4), (True, 6, 4, 4, 16), (False, -1, 8, 1, 1), (False, 9, 2, 1, 8),
     (True, -1, 16, 2, 64)])

@@ -56,6 +56,12 @@ DECODE = [
     (105, 64, 8, 4, 4, 100, "zero", True),
     (106, 128, 16, 2, 256, -1, "nan", True),
     (107, 64, 2, 1, 8, -1, "nan", True),
+    # KV head counts that are not a multiple of the 4 waves of a workgroup, so a
+    # worker's waves straddle workgroups; group 8 without splits
+    (108, 128, 12, 3, 16, -1, "nan", True),
+    (109, 128, 40, 5, 8, 50, "nan", False),
+    (110, 64, 6, 3, 16, -1, "nan", True),
+    (111, 128, 64, 8, 16, -1, "nan", False),
 ]
 
 
