@@ -48,7 +48,9 @@ METRIC = "decode KV-read GB/s (% HBM peak); prefill TFLOP/s (% bf16 MFMA peak)"
 FETCH_SCALE = 2.0
 WRITE_SCALE = 1.0
 CSRC = os.path.join(ROOT, "paged_kv_attention_plan_amd", "csrc")
-KERNEL_SOURCE = {"decode_kernel": "decode.hip", "prefill_kernel": "prefill.hip"}
+# the files whose text makes each kernel (its launch file and its device code)
+KERNEL_SOURCE = {"decode_kernel": ["decode.hip", "decode_body.cuh", "common.cuh"],
+                 "prefill_kernel": ["prefill.hip", "prefill_body.cuh", "common.cuh"]}
 
 DESCR = {
     "tiny_decode": "tiny decode: 4 requests, Hq 4 / Hk 2, D 64, page 16, kv_len U[1,100]",
@@ -74,8 +76,11 @@ DESCR = {
 
 def _source_sha(kernel):
     import hashlib
-    with open(os.path.join(CSRC, KERNEL_SOURCE[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCE[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_of(kernel, workload):
@@ -514,11 +519,15 @@ def secondary(name, dev, steps, warmup):
     if r.dense:
         res["gather_fresh_us"] = round(mean_ms(kt["append"]) * 1e3, 2)
         res["gather_with_prefix_us"] = r.gather_prefix_us()
-    if r.work["prefill_flops"]:
+    if r.work["prefill_flops"] and kt["prefill"]:
         pms = mean_ms(kt["prefill"])
         res["prefill_kernel_us"] = round(pms * 1e3, 2)
         res["prefill_TFLOPs_per_kernel"] = round(r.work["prefill_flops"] / (pms * 1e-3) / 1e12, 1)
         res["prefill_frac_mfma_peak"] = round(res["prefill_TFLOPs_per_kernel"] / MFMA_BF16_PEAK_TFS, 4)
+    elif r.work["prefill_flops"]:  # a mixed plan's one launch, timed as "decode"
+        fms = mean_ms(kt["decode"])
+        res["fused_decode_prefill_launch"] = True
+        res["prefill_TFLOPs_in_fused_launch"] = round(r.work["prefill_flops"] / (fms * 1e-3) / 1e12, 1)
     del r
     import torch
     torch.cuda.empty_cache()
@@ -564,10 +573,12 @@ def main():
         value, unit = w["kv_bytes"] / (ms * 1e-3) / 1e9, "GB/s"
         dec_ms = mean_ms(kt["decode"])
         achieved = w["decode_bytes"] / (dec_ms * 1e-3) / 1e9
+        # a mixed plan runs decode and prefill in one launch (mixed_kernel)
+        kname = "mixed_kernel" if w["prefill_flops"] and not kt["prefill"] else "decode_kernel"
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_of("decode_kernel", args.config),
-                "kernel": "decode_kernel", "kernel_us": round(dec_ms * 1e3, 2),
+                "traffic": traffic_of(kname, args.config) if kname in KERNEL_SOURCE else None,
+                "kernel": kname, "kernel_us": round(dec_ms * 1e3, 2),
                 "bytes_per_launch": w["decode_bytes"]}
     else:  # prefill only: FLOP per second, prefill kernel on bf16 MFMA
         value, unit = w["prefill_flops"] / (ms * 1e-3) / 1e12, "TFLOP/s"

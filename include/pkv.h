@@ -241,6 +241,8 @@ pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_byt
  * workspace must be the buffer of the last pkv_plan_upload (else PKV_E_STATE).
  * Decode rows whose keys span several chunks write fp32 partials into the
  * workspace and a merge kernel combines them by log-sum-exp (attn.workspace).
+ * A mixed plan with page_size >= 16 runs its decode rows and prompt rows in one
+ * launch (FlashInferMixedWrapper: both sub-plans in one step), the merge after it.
  * One upload serves any number of runs (one per layer); runs that overlap on one
  * workspace (two streams, no ordering) race on its partials.  Enqueued on stream. */
 pkv_status pkv_run(const pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
@@ -334,8 +336,9 @@ pkv_status pkv_context_only_views(int32_t batch, int32_t page_size, const int32_
  * counterpart).  While enabled, pkv_run, pkv_run_append and pkv_append_kv record a HIP event on the
  * stream before and after every kernel they launch with this plan.
  * pkv_timing_read waits for those events, returns for each kernel kind
- * ([0] append or dense gather, [1] decode, [2] split-KV merge, [3] prefill or dense
- * attention) the summed milliseconds
+ * ([0] append or dense gather, [1] decode, or the one launch of a mixed plan's decode
+ * and prefill work, [2] split-KV merge, [3] prefill or dense attention) the summed
+ * milliseconds
  * and the number of launches since the last read, and clears the record.
  * Events come from a pool the plan owns (created on first use, reused after a read). */
 pkv_status pkv_timing_enable(pkv_plan* plan, int32_t enable);

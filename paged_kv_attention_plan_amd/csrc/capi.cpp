@@ -370,28 +370,58 @@ pkv_status run_impl(const pkv_plan* plan, const void* q, const void* kv_cache_la
   // for its capacities, and the kernels read the step's counts from the header.
   const bool st = d.is_static;
   const int64_t* counts = st ? reinterpret_cast<const int64_t*>(ws) : nullptr;
-  if (st ? d.caps.dec_workers > 0 : d.n_workers > 0) {
+  const bool has_dec = st ? d.caps.dec_workers > 0 : d.n_workers > 0;
+  const bool has_pre = st ? d.caps.prefill_tiles > 0 : !d.prefill_tiles.empty();
+  pkv::DecodeArgs da{};
+  if (has_dec) {
     // a graph-static plan's worker table always has its capacity's entries
-    pkv::DecodeArgs a{};
-    a.pieces = reinterpret_cast<const pkv::DecodePieceMeta*>(ws + d.ws.off_decode_tiles);
-    a.rows = reinterpret_cast<const pkv::DecodeRowMeta*>(ws + d.ws.off_decode_rows);
-    a.work = reinterpret_cast<const int32_t*>(ws + d.ws.off_decode_work);
-    a.n_workers = (int32_t)(st ? d.caps.dec_workers : (int64_t)d.n_workers);
-    a.indices = indices;
-    a.q = static_cast<const uint16_t*>(q);
-    a.cache = static_cast<const uint16_t*>(kv_cache_layer);
-    a.out = static_cast<uint16_t*>(out);
-    a.lse = lse;
-    a.part_o = part_o;
-    a.part_lse = part_lse;
-    a.num_qo_heads = P.num_qo_heads;
-    a.num_kv_heads = P.num_kv_heads;
-    a.head_dim = P.head_dim;
-    a.page_size = P.page_size;
-    a.group = d.group;
-    a.scale_log2 = scale_log2;
+    da.pieces = reinterpret_cast<const pkv::DecodePieceMeta*>(ws + d.ws.off_decode_tiles);
+    da.rows = reinterpret_cast<const pkv::DecodeRowMeta*>(ws + d.ws.off_decode_rows);
+    da.work = reinterpret_cast<const int32_t*>(ws + d.ws.off_decode_work);
+    da.n_workers = (int32_t)(st ? d.caps.dec_workers : (int64_t)d.n_workers);
+    da.indices = indices;
+    da.q = static_cast<const uint16_t*>(q);
+    da.cache = static_cast<const uint16_t*>(kv_cache_layer);
+    da.out = static_cast<uint16_t*>(out);
+    da.lse = lse;
+    da.part_o = part_o;
+    da.part_lse = part_lse;
+    da.num_qo_heads = P.num_qo_heads;
+    da.num_kv_heads = P.num_kv_heads;
+    da.head_dim = P.head_dim;
+    da.page_size = P.page_size;
+    da.group = d.group;
+    da.scale_log2 = scale_log2;
+  }
+  pkv::PrefillArgs pa{};
+  if (has_pre) {
+    pa.tiles = reinterpret_cast<const pkv_prefill_tile*>(ws + d.ws.off_prefill_tiles);
+    pa.n_tiles = (int32_t)(st ? d.caps.prefill_tiles : (int64_t)d.prefill_tiles.size());
+    pa.counts = counts;
+    pa.indices = indices;
+    pa.q = static_cast<const uint16_t*>(q);
+    pa.cache = static_cast<const uint16_t*>(kv_cache_layer);
+    pa.out = static_cast<uint16_t*>(out);
+    pa.lse = lse;
+    pa.num_qo_heads = P.num_qo_heads;
+    pa.num_kv_heads = P.num_kv_heads;
+    pa.head_dim = P.head_dim;
+    pa.page_size = P.page_size;
+    pa.group = d.group;
+    pa.causal = P.causal ? 1 : 0;
+    pa.window_left = P.window_left;
+    pa.scale_log2 = scale_log2;
+  }
+  // A mixed step runs its decode waves and prefill tiles in one launch (the
+  // two write disjoint tokens); the merge of split decode rows follows.
+  const bool fused = has_dec && has_pre && pkv::mixed_launch_fits(da, pa);
+  if (fused) {
     PKV_HIP(timing_mark(plan, s, kDecode, true));
-    PKV_HIP(pkv::launch_decode(a, s));
+    PKV_HIP(pkv::launch_mixed(da, pa, s));
+    PKV_HIP(timing_mark(plan, s, kDecode, false));
+  } else if (has_dec) {
+    PKV_HIP(timing_mark(plan, s, kDecode, true));
+    PKV_HIP(pkv::launch_decode(da, s));
     PKV_HIP(timing_mark(plan, s, kDecode, false));
   }
   if (st ? d.caps.merges > 0 : !d.merges.empty()) {
@@ -413,26 +443,9 @@ pkv_status run_impl(const pkv_plan* plan, const void* q, const void* kv_cache_la
     PKV_HIP(pkv::launch_merge(a, s));
     PKV_HIP(timing_mark(plan, s, kMerge, false));
   }
-  if (st ? d.caps.prefill_tiles > 0 : !d.prefill_tiles.empty()) {
-    pkv::PrefillArgs a{};
-    a.tiles = reinterpret_cast<const pkv_prefill_tile*>(ws + d.ws.off_prefill_tiles);
-    a.n_tiles = (int32_t)(st ? d.caps.prefill_tiles : (int64_t)d.prefill_tiles.size());
-    a.counts = counts;
-    a.indices = indices;
-    a.q = static_cast<const uint16_t*>(q);
-    a.cache = static_cast<const uint16_t*>(kv_cache_layer);
-    a.out = static_cast<uint16_t*>(out);
-    a.lse = lse;
-    a.num_qo_heads = P.num_qo_heads;
-    a.num_kv_heads = P.num_kv_heads;
-    a.head_dim = P.head_dim;
-    a.page_size = P.page_size;
-    a.group = d.group;
-    a.causal = P.causal ? 1 : 0;
-    a.window_left = P.window_left;
-    a.scale_log2 = scale_log2;
+  if (has_pre && !fused) {
     PKV_HIP(timing_mark(plan, s, kPrefill, true));
-    PKV_HIP(pkv::launch_prefill(a, s));
+    PKV_HIP(pkv::launch_prefill(pa, s));
     PKV_HIP(timing_mark(plan, s, kPrefill, false));
   }
   return PKV_OK;

@@ -108,5 +108,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// Decode waves and prefill tiles of a mixed step in one grid (decode
+// workgroups first).  Only where mixed_launch_fits: paged K/V with
+// page_size >= 16 and one head_dim for both.
+bool mixed_launch_fits(const DecodeArgs& da, const PrefillArgs& pa);
+hipError_t launch_mixed(const DecodeArgs& da, const PrefillArgs& pa, hipStream_t stream);
 
 }  // namespace pkv
