@@ -41,7 +41,7 @@
 namespace pkv {
 namespace dec {
 
-constexpr int kWaves = 4;  // wavefronts (tiles) per workgroup
+constexpr int kWaves = 4;  // waves per workgroup
 
 // Loads per iteration (each for K and V).  With 8 query heads per KV head the
 // accumulators take twice the registers, so the load buffers are halved to
