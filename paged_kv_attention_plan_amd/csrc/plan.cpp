@@ -30,7 +30,6 @@
 #include <algorithm>
 #include <cstring>
 #include <numeric>
-#include <unordered_set>
 
 namespace pkv {
 namespace {
@@ -402,12 +401,29 @@ pkv_status build_plan(const pkv_plan_params& P, int32_t num_cus, int32_t batch,
     }
   }
   {
-    std::unordered_set<int64_t> seen;
-    seen.reserve(plan.slots.size() * 2 + 1);
-    for (size_t i = 0; i < plan.slots.size(); ++i) {
-      if (!seen.insert(plan.slots[i]).second) {
-        err = "two appended tokens map to cache slot " + std::to_string(plan.slots[i]) +
-              " (token " + std::to_string(i) + ")";
+    // Every written page entry of a row takes an interval of offsets [lo, hi]
+    // of its page; two tokens share a slot exactly when two intervals of the
+    // same page overlap.  Sorting the intervals (about T / ps + rows of them)
+    // finds that without a set of all T slots.
+    struct Iv { int64_t page; int32_t lo, hi; int64_t tok; };
+    std::vector<Iv> ivs;
+    for (int32_t r = 0; r < batch; ++r) {
+      const int64_t n = kv_len[r], L = q_len[r];
+      for (int64_t p = n - L; p < n;) {
+        const int64_t e = p / ps, pend = std::min(n, (e + 1) * ps);
+        ivs.push_back({kv_indices[kv_indptr[r] + e], (int32_t)(p % ps),
+                       (int32_t)((pend - 1) % ps), q_start[r] + (p - (n - L))});
+        p = pend;
+      }
+    }
+    std::sort(ivs.begin(), ivs.end(), [](const Iv& a, const Iv& b) {
+      return a.page != b.page ? a.page < b.page : a.lo < b.lo;
+    });
+    for (size_t i = 1; i < ivs.size(); ++i) {
+      if (ivs[i].page == ivs[i - 1].page && ivs[i].lo <= ivs[i - 1].hi) {
+        err = "two appended tokens map to cache slot " +
+              std::to_string(ivs[i].page * ps + ivs[i].lo) + " (token " +
+              std::to_string(ivs[i].tok) + ")";
         return PKV_E_CONFLICT;
       }
     }

@@ -265,6 +265,37 @@ def test_error_conflicting_write_slots():
     assert _err(lambda: pkv.plan_create(p, None, ind, idx, lpl)) == pkv.E_CONFLICT
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_write_slot_conflicts_match_brute_force(seed):
+    """The planner rejects a step with PKV_E_CONFLICT exactly when two of its
+    query tokens' write slots (page * ps + offset, kv.plan) coincide, checked
+    here with a set of all slots.  Rows draw pages from a small pool, with
+    repeats inside a row and across rows, so both outcomes occur."""
+    rng = np.random.default_rng(300 + seed)
+    ps = int(rng.choice([1, 2, 4, 8]))
+    B = int(rng.integers(2, 7))
+    kv = rng.integers(1, 6 * ps + 1, size=B)
+    ql = np.array([rng.integers(1, k + 1) for k in kv])
+    npg = (kv + ps - 1) // ps
+    pool = int(rng.integers(max(2, int(npg.max())), 8 * int(npg.sum()) + 3))
+    idx = rng.integers(0, pool, size=int(npg.sum())).astype(np.int32)
+    ind = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+    lpl = ((kv - 1) % ps + 1).astype(np.int32)
+    qo = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+    slots = []
+    for r in range(B):
+        for p_ in range(int(kv[r] - ql[r]), int(kv[r])):
+            slots.append(int(idx[ind[r] + p_ // ps]) * ps + p_ % ps)
+    dup = len(set(slots)) < len(slots)
+    p = pkv.plan_params("prefill", num_qo_heads=2, num_kv_heads=1, head_dim=64, page_size=ps,
+                        max_pages=pool, num_cus=1)
+    if dup:
+        assert _err(lambda: pkv.plan_create(p, qo, ind, idx, lpl)) == pkv.E_CONFLICT
+    else:
+        plan = pkv.plan_create(p, qo, ind, idx, lpl)
+        assert list(plan.write_slots()) == slots
+
+
 def test_shared_pages_for_reading_are_allowed():
     ind = np.array([0, 2, 4], dtype=np.int32)
     idx = np.array([0, 2, 1, 3], dtype=np.int32)  # page 0..: rows share nothing but may
