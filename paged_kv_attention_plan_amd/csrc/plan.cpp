@@ -98,8 +98,10 @@ void make_prefill_tiles(const pkv_plan_params& P, const std::vector<int32_t>& ro
   const int32_t Hk = P.num_kv_heads;
   const int64_t bt = 128 / (P.num_qo_heads / Hk);
   const int64_t w = P.window_left;
-  struct Item { int64_t keys; int32_t r, b, hk; pkv_prefill_tile t; };
-  std::vector<Item> items;
+  // Every KV head of a query block has the block's key range, and the head is
+  // the last tie-breaker: sort the blocks, then emit their heads in order.
+  struct Block { int64_t keys; int32_t r, b; int32_t qs, qc, lo, hi; };
+  std::vector<Block> blocks;
   for (int32_t r : rows) {
     const int64_t n = kv_len[r], L = q_len[r];
     for (int64_t b = 0; b * bt < L; ++b) {
@@ -107,30 +109,32 @@ void make_prefill_tiles(const pkv_plan_params& P, const std::vector<int32_t>& ro
       const int64_t p0 = n - L + qs, p1 = p0 + qc - 1;
       const int64_t lo = w < 0 ? 0 : std::max<int64_t>(0, p0 - w);
       const int64_t hi = P.causal ? p1 : n - 1;
-      for (int32_t hk = 0; hk < Hk; ++hk) {
-        pkv_prefill_tile t{};
-        t.row = r;
-        t.kv_head = hk;
-        t.q_start = (int32_t)qs;
-        t.q_count = (int32_t)qc;
-        t.kv_lo = (int32_t)lo;
-        t.kv_hi = (int32_t)hi;
-        t.page_base = page_base(r);
-        t.q_base = q_start[r];
-        t.kv_len = (int32_t)n;
-        t.q_len = (int32_t)L;
-        items.push_back({hi - lo + 1, r, (int32_t)b, hk, t});
-      }
+      blocks.push_back({hi - lo + 1, r, (int32_t)b, (int32_t)qs, (int32_t)qc, (int32_t)lo,
+                        (int32_t)hi});
     }
   }
-  std::sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
+  std::sort(blocks.begin(), blocks.end(), [](const Block& a, const Block& b) {
     if (a.keys != b.keys) return a.keys > b.keys;
     if (a.r != b.r) return a.r < b.r;
-    if (a.b != b.b) return a.b < b.b;
-    return a.hk < b.hk;
+    return a.b < b.b;
   });
-  tiles.reserve(items.size());
-  for (auto& it : items) tiles.push_back(it.t);
+  tiles.reserve(blocks.size() * Hk);
+  for (const Block& bl : blocks) {
+    pkv_prefill_tile t{};
+    t.row = bl.r;
+    t.q_start = bl.qs;
+    t.q_count = bl.qc;
+    t.kv_lo = bl.lo;
+    t.kv_hi = bl.hi;
+    t.page_base = page_base(bl.r);
+    t.q_base = q_start[bl.r];
+    t.kv_len = kv_len[bl.r];
+    t.q_len = q_len[bl.r];
+    for (int32_t hk = 0; hk < Hk; ++hk) {
+      t.kv_head = hk;
+      tiles.push_back(t);
+    }
+  }
 }
 
 
