@@ -109,8 +109,9 @@ typedef struct pkv_plan_params {
                                    device (the workspace page: plan size depends on the SM count) */
   int64_t max_pages;            /* pages in the layer slice; page ids must be below it */
   int32_t decode_waves_per_cu;  /* decode waves per CU the split-KV partition balances over
-                                   (workers = num_cus * this / num_kv_heads); 0 = 4 for
-                                   group 1, 2, 4 and 16 for group 8 */
+                                   (workers = num_cus * this / num_kv_heads, and for a
+                                   graph-static plan at most static_max_page_entries); 0 = 4
+                                   for group 1, 2, 4 and 16 for group 8 */
   int32_t decode_min_chunk_pages; /* smallest per-worker share of a step's pages; 0 = 8 */
   /* Graph-static mode (attn.wrappers: static buffers for graph capture, sized by
    * batch_size / max_num_pages / max_total_tokens).  All three 0: off.  All three > 0:

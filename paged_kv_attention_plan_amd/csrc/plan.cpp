@@ -48,12 +48,16 @@ constexpr int64_t kPieceCost = 2;
 // HBM and one wave per SIMD keeps enough loads in flight; sixteen for group 8,
 // where the kernel is bound by its vector ALU and more, shorter pieces keep
 // every SIMD busy.  (Measured on MI355X over waves per CU 4, 8, 12 and 16.)
+// A graph-static plan has no more workers than page entries (each worker holds
+// at least one page), so its capacity grid stays small for small capacities.
 int64_t decode_workers(const pkv_plan_params& P, int64_t num_cus) {
   const int64_t g = P.num_qo_heads / P.num_kv_heads;
   const int64_t waves_per_cu = P.decode_waves_per_cu > 0 ? P.decode_waves_per_cu
                                : g == 8                  ? 16
                                                          : 4;
-  return std::max<int64_t>(1, num_cus * waves_per_cu / P.num_kv_heads);
+  int64_t w = std::max<int64_t>(1, num_cus * waves_per_cu / P.num_kv_heads);
+  if (P.static_max_page_entries > 0) w = std::min(w, P.static_max_page_entries);
+  return w;
 }
 
 // Pour rows of `pages` (in order) into workers of capacity `cap`; emit(row
