@@ -25,7 +25,7 @@ Policy (the same rules the header documents):
                 needs at most W workers.  Per row pieces in order, per piece
                 tiles head-minor.  Rows with more than one piece get
                 Hk * n_pieces consecutive partial slots, head-major.
-  prefill rows  blocks of 128 // group query tokens; per block keys
+  prefill rows  blocks of 192 // group query tokens; per block keys
                 [lo(first token), hi(last token)]; tiles sorted by key count
                 descending, ties by (row, block, head).
 """
@@ -120,12 +120,17 @@ def decode_policy(layout, rows, *, page_size, num_kv_heads, window_left, num_cus
     return tiles, merges, cap, slot, work
 
 
+# (query head, token) pairs of one prefill tile under the library's documented
+# policy.
+TILE_PAIRS = 192
+
+
 def prefill_policy(layout, rows, *, num_qo_heads, num_kv_heads, causal, window_left, qo_indptr,
                    kv_indptr):
     """Expected prefill tiles as tuples
     (row, kv_head, q_start, q_count, kv_lo, kv_hi, page_base, q_base, kv_len, q_len)."""
     group = num_qo_heads // num_kv_heads
-    bt = 128 // group
+    bt = TILE_PAIRS // group
     items = []
     for r in rows:
         n, L = layout[r].kv_len, layout[r].q_len

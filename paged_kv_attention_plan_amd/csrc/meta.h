@@ -9,6 +9,11 @@
 
 namespace pkv {
 
+// (query head, token) pairs of one prefill tile: the planner cuts each prompt
+// row into blocks of kPrefillTilePairs / group query tokens per KV head, and
+// the prefill kernel's four waves take 48 pairs each.
+constexpr int kPrefillTilePairs = 192;
+
 // One decode row (a row with one query token), in decode-piece order.
 struct DecodeRowMeta {
   int32_t page_base;  // paged_kv_indptr[row]

@@ -21,8 +21,9 @@
 //          pages plus one piece cost per row, for which the pour uses at most
 //          W workers.  A row cut into n > 1 pieces owns Hk * n consecutive
 //          partial slots (head-major) and one merge per head.
-//  prefill Query tokens are taken in blocks of 128/group so a block fills the
-//          128 rows of a kernel tile; a block's keys are [lo of its first token,
+//  prefill Query tokens are taken in blocks of kPrefillTilePairs/group (192/group)
+//          so a block fills the 192 (head, token) pairs of a kernel tile; a
+//          block's keys are [lo of its first token,
 //          hi of its last token].  Tiles are ordered by key count, largest first
 //          (ties: row, block, KV head), so the longest work is dispatched first.
 #include "plan.h"
@@ -90,7 +91,7 @@ std::string fmt_row(const char* what, int64_t r) {
 }
 
 // Prefill tiles of the given rows (FlashInferPrefillWrapper.plan): blocks of
-// 128 / group query tokens per KV head, keys [lo(first token), hi(last token)],
+// kPrefillTilePairs / group query tokens per KV head, keys [lo(first token), hi(last token)],
 // sorted by key count descending, ties by (row, block, head).  page_base(r) is
 // where row r's keys start: its first page-table entry, or its first dense row.
 template <class PageBase>
@@ -100,7 +101,7 @@ void make_prefill_tiles(const pkv_plan_params& P, const std::vector<int32_t>& ro
                         std::vector<pkv_prefill_tile>& tiles) {
   if (rows.empty()) return;
   const int32_t Hk = P.num_kv_heads;
-  const int64_t bt = 128 / (P.num_qo_heads / Hk);
+  const int64_t bt = kPrefillTilePairs / (P.num_qo_heads / Hk);
   const int64_t w = P.window_left;
   // Every KV head of a query block has the block's key range, and the head is
   // the last tie-breaker: sort the blocks, then emit their heads in order.
@@ -180,8 +181,9 @@ pkv_status check_params(const pkv_plan_params& p, std::string& err) {
     err = "decode rows need num_qo_heads / num_kv_heads in {1, 2, 4, 8} (got " + std::to_string(g) + ")";
     return PKV_E_UNSUPPORTED;
   }
-  if (p.kind != PKV_KIND_DECODE && (128 % g) != 0) {
-    err = "prefill rows need num_qo_heads / num_kv_heads to divide 128 (got " + std::to_string(g) + ")";
+  if (p.kind != PKV_KIND_DECODE && (kPrefillTilePairs % g) != 0) {
+    err = "prefill rows need num_qo_heads / num_kv_heads to divide " +
+          std::to_string(kPrefillTilePairs) + " (got " + std::to_string(g) + ")";
     return PKV_E_UNSUPPORTED;
   }
   if (p.kind == PKV_KIND_MIXED && p.max_prefill_rows < 0) {
@@ -253,7 +255,7 @@ void layout_workspace(PlanData& plan) {
 // parameters); every worker boundary cuts at most one row, so at most
 // rows + W - 1 pieces; a split row of n pieces owns Hk * n partial slots, so at
 // most Hk * (rows + W) slots; a row splits into at most Hk merges.  Prefill
-// tiles: Hk per block of 128 / group tokens, at most
+// tiles: Hk per block of kPrefillTilePairs / group tokens, at most
 // Hk * (ceil(tokens / block) + rows).
 PlanData::Caps static_caps(const pkv_plan_params& P, int32_t num_cus) {
   PlanData::Caps c;
@@ -267,7 +269,7 @@ PlanData::Caps static_caps(const pkv_plan_params& P, int32_t num_cus) {
     c.n_slots = Hk * c.dec_pieces;
   }
   if (P.kind != PKV_KIND_DECODE) {
-    const int64_t bt = 128 / g;
+    const int64_t bt = kPrefillTilePairs / g;
     const int64_t rows = P.kind == PKV_KIND_MIXED ? std::min<int64_t>(B, P.max_prefill_rows) : B;
     c.prefill_tiles = Hk * ((T + bt - 1) / bt + rows);
   }

@@ -5,23 +5,31 @@
 // Causal ragged prefill over a paged KV cache (FlashInferPrefillWrapper.run on
 // the mstar attn.wrappers page; the [cached prefix | fresh tokens] sequence of
 // attn.dense).  A dense contraction, so both products run on bf16 MFMA
-// (v_mfma_f32_32x32x16_bf16) with fp32 accumulation.
+// (v_mfma_f32_16x16x32_bf16) with fp32 accumulation.
 //
-// A workgroup (4 waves) owns one tile: a row, a KV head and a block of BT =
-// 128/group query tokens, i.e. 128 (query head, token) pairs that all read the
-// same K/V.  Wave w takes pairs 32w..32w+31.  Keys are consumed 64 at a time:
-// the workgroup gathers the 64 key rows of K and V from their pages into LDS,
-// both as rows [key][d], and every wave then computes
-//   S^T (64 keys x 32 queries) = K . Q^T       (A = K from LDS, B = Q in registers)
+// A workgroup (4 waves) owns one tile: a row, a KV head and a block of
+// BT = 64*NQB/group query tokens, i.e. 64*NQB (query head, token) pairs that
+// all read the same K/V.  Wave w takes NQB blocks of 16 pairs.  Keys are
+// consumed 32 at a time: the workgroup gathers the 32 key rows of K and V from
+// their pages into LDS, both as rows [key][d], and every wave computes, per
+// query block,
+//   S^T (32 keys x 16 queries) = K . Q^T       (A = K from LDS, B = Q in registers)
 //   P = exp2(S*scale*log2e - m)                (online softmax, fp32, per query column)
-//   O^T (D x 32 queries)     += V^T . P^T      (A = V^T, read transposed from LDS
+//   O^T (D x 16 queries)     += V^T . P^T      (A = V^T, read transposed from LDS
 //                                                by ds_read_b64_tr_b16; B = P as bf16)
-// With S^T a lane holds one query column, so the row max needs a single
-// cross-half exchange and the per-query rescale is a per-lane scalar.
+// Each K or V fragment read from LDS feeds NQB matrix instructions, so the LDS
+// read traffic per FLOP falls as 1/NQB.  NQB = 3 (48 queries per wave) fits at
+// two waves per SIMD because K and V are copied from memory straight into LDS
+// (global_load_lds_dwordx4), NBUF-1 steps ahead into a ring of NBUF buffers,
+// with no registers held for the copies in flight.
+//
+// In the 16x16x32 layouts a lane holds one query column (lane % 16) and four
+// keys 4*(lane/16) .. +3 of every 16-key block; the column max and sum need two
+// cross-row exchanges (v_permlane16_swap, v_permlane32_swap).
 //
 // The running max is only moved when some query's new maximum exceeds it by
 // more than 2^8 (in exp2 units): P stays <= 256, harmless in fp32 and bf16,
-// and the O rescale (64 multiplies per lane) is skipped on most key tiles.
+// and the O rescale is skipped on most key tiles.
 #include <type_traits>
 
 #include "common.cuh"
@@ -32,26 +40,17 @@ namespace pre {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr float kRescaleSlack = 8.f;  // log2 units: P may reach 2^8 before O is rescaled
-#ifndef PKV_PREFILL_AHEAD
-#define PKV_PREFILL_AHEAD 3
-#endif
-#ifndef PKV_PREFILL_VALU_QK
-#define PKV_PREFILL_VALU_QK 7
-#endif
-#ifndef PKV_PREFILL_VALU_PV
-#define PKV_PREFILL_VALU_PV 2
-#endif
-constexpr int kAhead = PKV_PREFILL_AHEAD;      // LDS fragments in flight ahead of the MFMAs
-constexpr int kValuQK = PKV_PREFILL_VALU_QK;   // VALU slots per MFMA while S is formed
-constexpr int kValuPV = PKV_PREFILL_VALU_PV;   // VALU slots per MFMA while O is updated
+constexpr int kTilePairs = kPrefillTilePairs;  // (query head, token) pairs per tile
+constexpr int kNqb = kTilePairs / 64;          // 16-pair query blocks per wave
+static_assert(kTilePairs % 64 == 0, "tile pairs must be a multiple of 64");
 
-__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+constexpr float kRescaleSlack = 8.f;  // log2 units: P may reach 2^8 before O is rescaled
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
@@ -60,7 +59,57 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
 }
 
+// x combined with the same register of lane ^ 16 (v_permlane16_swap: odd and
+// even rows of 16 lanes trade places) or of lane ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float max_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+#ifndef PKV_PREFILL_KA
+#define PKV_PREFILL_KA 2
+#endif
+#ifndef PKV_PREFILL_NBUF
+#define PKV_PREFILL_NBUF 4
+#endif
+
+// One 16-byte-per-lane copy from memory straight into LDS: lane l's 16 bytes
+// at sbase + voff go to LDS byte m0 + 16 l (global_load_lds_dwordx4).  The
+// compiler does not see these copies; their completion is awaited with
+// wait_copies (vmcnt counts them with the wave's other vector memory reads,
+// which return in issue order).
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               ::"v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_flat(const void* p, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(p), "s"(m0) : "memory", "m0");
+}
+// Wait until at most N of this wave's vector memory reads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // ds_read_b64_tr_b16: in each group of 16 lanes, lane L receives element L%4 of
 // the 4-element (8-byte) rows addressed by lanes L/4, L/4+4, L/4+8, L/4+12, in
@@ -74,29 +123,39 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 
-// WAVE_PAGE: page_size >= 16, so the 16 keys a wave stages per tile lie in one
+// WAVE_PAGE: page_size >= 16, so the 8 keys a wave stages per step lie in one
 // page -- its id is a scalar load and the loads use a scalar base.
 // DENSE (with WAVE_PAGE): the keys are contiguous rows of k_dense / v_dense
 // starting at the tile's page_base; the row acts as one page.
 // Tile `tile` of the prefill tile list, by a workgroup of 256 threads.
 template <int D, bool WAVE_PAGE, bool DENSE>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
-  constexpr int BN = 64;              // keys per tile
-  constexpr int KSTEPS = D / 16;      // MFMA steps over head_dim for S
-  constexpr int DBLK = D / 32;        // 32-row output blocks over head_dim
+  constexpr int NQB = kNqb;
+  constexpr int BN = 32;              // keys per step
+  constexpr int KSTEPS = D / 32;      // MFMA steps over head_dim for S
+  constexpr int DBLK = D / 16;        // 16-row output blocks over head_dim
   constexpr int SEGS = D / 8;         // 16-byte segments of a key row
-  constexpr int KPT = BN * SEGS / 256;  // key rows each thread stages per tile
-  // LDS row strides (elements), chosen free of bank conflicts (64 banks of 4
-  // bytes): the 16 lanes of a K row read start 4 (D=128) or 36 (D=64) banks
-  // apart; a transposed V read serves 32 lanes at once, 4 rows x 2 column
-  // groups of 8 banks, with rows 16 (D=128) or 48 (D=64) banks apart, so the
-  // 32 lanes touch each bank once.
-  constexpr int KS = D + 8;
-  constexpr int VS = D + 32;
-  constexpr int KBUF = BN * KS, VBUF = BN * VS;
-  // Two LDS buffers: tile t lives in buffer t % 2.
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * KBUF];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2 * VBUF];
+  constexpr int KW = BN / 4;          // keys each wave copies per step
+  constexpr int NI = KW * D * 2 / 1024; // 1 KB copies per wave per step, per tensor
+  constexpr int RPI = 1024 / (2 * D); // key rows per 1 KB copy
+  constexpr int ROWB = 2 * D;         // LDS row bytes (no padding)
+  constexpr int BUFB = BN * ROWB;     // bytes of one step's K (or V)
+  constexpr int NBUF = PKV_PREFILL_NBUF;
+  constexpr int PF = NBUF - 1;        // steps a copy runs ahead of its first read
+  static_assert(NBUF >= 3, "the scores of step i+1 are read in step i");
+  // K and V reach LDS straight from memory (global_load_lds_dwordx4: a wave's
+  // copy fills 1 KB of LDS, 16 bytes per lane in lane order), so rows cannot
+  // be padded; instead the 16-byte segments of a row are XOR-swizzled.
+  //  K, row r: segment c at c ^ kswz(r).  The 16 lanes reading one column of a
+  //    16-key block (rows r0 .. r0+15) then touch 16 different segments.
+  //  V, row r: segment c at c ^ vswz(r).  A transposed read serves 32 lanes,
+  //    8 rows x 2 segments; the swizzle moves the 8 rows' segment pairs apart.
+  // (D=64 rows are half the 64 banks, so row pairs share the swizzle.)
+  auto kswz = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto vswz = [](int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); };
+  // NBUF LDS buffers: step t lives in buffer t % NBUF.
+  __shared__ __attribute__((aligned(1024))) uint8_t sK[NBUF * BUFB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV[NBUF * BUFB];
 
   if (a.counts != nullptr && (int64_t)tile >= as_const4(a.counts)[2]) return;
   const pkv_prefill_tile* tp = a.tiles + tile;
@@ -112,7 +171,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
 
   const int Hq = a.num_qo_heads;
   const int g = a.group;
-  const int BT = 128 / g;
+  const int BT = kTilePairs / g;
   const int ps = a.page_size;
   const int ps_log2 = __builtin_ctz(ps);
   const int row_elems = a.num_kv_heads * D;
@@ -124,325 +183,352 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int jcol = lane & 31;
-  const int half = lane >> 5;
-  const int mrow = wave * 32 + jcol;
-  const int hl = mrow / BT;
-  const int tl = mrow - hl * BT;
-  const int qh = hk * g + hl;
-  const bool qvalid = tl < q_count;
-  const int token = q_base + q_start + tl;
-  const int pos = kv_len - q_len + q_start + tl;  // sequence position of this query
-  const int hi_j = causal ? (pos < kv_len - 1 ? pos : kv_len - 1) : kv_len - 1;
-  const int lo_j = wl >= 0 ? pos - wl : 0;
+  const int li = lane & 15;   // query column inside a block; key row of a K fragment
+  const int lg = lane >> 4;   // row group: keys 4 lg .. 4 lg + 3 of each 16-key block
 
-  // Q^T operand: k-step s uses d = 16 s + 8 half .. +7 of this lane's query.
-  u32x4_t qreg[KSTEPS];
-  {
-    const uint16_t* qp = a.q + ((int64_t)token * Hq + qh) * D + 8 * half;
+  // Query blocks of this wave: pair m = 16 (NQB wave + b) + li is query head
+  // hk*g + m / BT at token m % BT of the tile.
+  auto pair_of = [&](int b, int& qh, int& tl) {
+    const int m = 16 * (NQB * wave + b) + li;
+    const int hl = m / BT;
+    tl = m - hl * BT;
+    qh = hk * g + hl;
+  };
+  // Sequence position of query block b of this lane; keys [pos - wl, pos]
+  // (causal) are visible.  Recomputed where needed (masked steps only).
+  auto pos_of = [&](int b) {
+    int qh, tl;
+    pair_of(b, qh, tl);
+    return kv_len - q_len + q_start + tl;
+  };
+
+  // Q^T operand: k-step s uses d = 32 s + 8 lg .. +7 of this lane's query.
+  u32x4_t qreg[NQB][KSTEPS];
+#pragma unroll
+  for (int b = 0; b < NQB; ++b) {
+    int qh, tl;
+    pair_of(b, qh, tl);
+    const uint16_t* qp = a.q + ((int64_t)(q_base + q_start + tl) * Hq + qh) * D + 8 * lg;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      if (qvalid) qreg[s] = *reinterpret_cast<const u32x4_t*>(qp + 16 * s);
-      else qreg[s] = u32x4_t{0u, 0u, 0u, 0u};
+      if (tl < q_count) qreg[b][s] = *reinterpret_cast<const u32x4_t*>(qp + 32 * s);
+      else qreg[b][s] = u32x4_t{0u, 0u, 0u, 0u};
     }
   }
 
-  f32x16_t oacc[DBLK];
+  f32x4_t oacc[NQB][DBLK];
 #pragma unroll
-  for (int b = 0; b < DBLK; ++b) oacc[b] = f32x16_t{};
-  float m_run = -1e30f, l_run = 0.f;  // m_run in exp2 units (scaled)
+  for (int b = 0; b < NQB; ++b)
+#pragma unroll
+    for (int d = 0; d < DBLK; ++d) oacc[b][d] = f32x4_t{};
+  float m_run[NQB], l_run[NQB];  // m_run in exp2 units (scaled)
+#pragma unroll
+  for (int b = 0; b < NQB; ++b) {
+    m_run[b] = -1e30f;
+    l_run[b] = 0.f;
+  }
 
   // Block-wide query position bounds, for deciding which key tiles need masks.
   const int p_first = kv_len - q_len + q_start;
   const int p_last = p_first + q_count - 1;
 
-  // Staging map: thread -> (segment, key group of KPT keys).  The 16 keys of a
-  // wave are [16*wave, 16*wave + 16) of the tile.
-  const int seg = threadIdx.x % SEGS;
-  const int kg = threadIdx.x / SEGS;
   const int kstart = kv_lo & ~(BN - 1);
   const int kend = kv_hi + 1;
   const int ntiles = (kend - kstart + BN - 1) / BN;
   const_as4_ptr<int32_t> cidx = as_const4(a.indices);
   const uint32_t row_bytes = (uint32_t)row_elems * 2u;
-  const int64_t head_bytes = (int64_t)hk * D * 2;
+  const uint32_t head_bytes = (uint32_t)hk * D * 2u;
 
-  // Key i of this thread in tile t (clamped to the last tile and the last key,
-  // so addresses stay inside the row; keys past the row are masked later).
-  auto key_of = [&](int t, int i) {
-    t = t < ntiles ? t : ntiles - 1;
-    const int key = kstart + t * BN + kg * KPT + i;
-    return key < kv_len ? key : kv_len - 1;
+  // Copy map: copy j of wave w fills rows KW*w + RPI*j + lane/SEGS of the step,
+  // physical segment lane % SEGS, with the source segment that the swizzle
+  // puts there.  src_k/src_v: the lane's byte offset inside a key row.
+  // (recomputed at each issue: a few VALU per step instead of 3*NI live registers)
+  auto copy_src = [&](int j, bool v, int& rwj) -> uint32_t {
+    rwj = RPI * j + lane / SEGS;
+    const int r = KW * wave + rwj;
+    return head_bytes + 16u * (uint32_t)((lane % SEGS) ^ (v ? vswz(r) : kswz(r)));
   };
-  // WAVE_PAGE: the wave's 16 keys k0 .. k0+15 (k0 a multiple of 16) lie in
-  // one page; the first is clamped to the row's last key to choose the page.
-  auto wave_key0 = [&](int t) {
+  const uint32_t lds_k = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(sK);
+  const uint32_t lds_v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)(sV);
+
+  // Issue the copies of step t (clamped to the last step, and each key to the
+  // row's last key, so addresses stay inside the row; keys past the row are
+  // masked later) into buffer t % NBUF.  Every call issues exactly 2*NI copies
+  // per wave: the waits below count on it.
+  auto issue = [&](int t, int buf) {
     t = t < ntiles ? t : ntiles - 1;
-    return kstart + t * BN + 16 * wave;
-  };
-  auto load_pids = [&](int t, int (&pid)[KPT]) {
-    if constexpr (DENSE) {
-      pid[0] = 0;  // no page table
-    } else if constexpr (WAVE_PAGE) {
-      const int k0 = wave_key0(t);
-      const int k0c = k0 < kv_len ? k0 : kv_len - 1;
-      pid[0] = cidx[page_base + (k0c >> ps_log2)];  // uniform: scalar load
-    } else {
+    const int k0 = kstart + t * BN + KW * wave;        // multiple of KW
+    const int kb0 = k0 < kv_len ? k0 : kv_len - 1;    // first key actually read
+    const int room = kv_len - 1 - kb0;                // keys after kb0 in the row
+    const uint32_t mk = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(lds_k + buf * BUFB + KW * wave * ROWB));
+    const uint32_t mv = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(lds_v + buf * BUFB + KW * wave * ROWB));
+    if constexpr (DENSE || WAVE_PAGE) {
+      // The wave's KW keys lie in one page (or one dense row): a uniform base.
+      const char* kbase;
+      if constexpr (DENSE) {
+        kbase = reinterpret_cast<const char*>(a.k_dense) + ((int64_t)page_base + kb0) * row_bytes;
+      } else {
+        const int pid = cidx[page_base + (kb0 >> ps_log2)];  // uniform: scalar load
+        kbase = reinterpret_cast<const char*>(a.cache) + (int64_t)pid * page_elems * 2 +
+                (int64_t)(kb0 & (ps - 1)) * row_bytes;
+      }
+      const char* vbase = DENSE ? reinterpret_cast<const char*>(a.v_dense) +
+                                      ((int64_t)page_base + kb0) * row_bytes
+                                : kbase + (int64_t)v_off * 2;
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) pid[i] = cidx[page_base + (key_of(t, i) >> ps_log2)];
+      for (int j = 0; j < NI; ++j) {
+        int rwj;
+        const uint32_t src = copy_src(j, false, rwj);
+        dma16((uint32_t)min(rwj, room) * row_bytes + src, kbase, mk + 1024u * j);
+      }
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        int rwj;
+        const uint32_t src = copy_src(j, true, rwj);
+        dma16((uint32_t)min(rwj, room) * row_bytes + src, vbase, mv + 1024u * j);
+      }
+    } else {
+      // Pages shorter than the wave's keys: a page id per lane.
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv)
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          int rwj;
+          const uint32_t src = copy_src(j, kv != 0, rwj);
+          const int key = kb0 + min(rwj, room);
+          const int pid = cidx[page_base + (key >> ps_log2)];
+          const char* p = reinterpret_cast<const char*>(a.cache) + (int64_t)pid * page_elems * 2 +
+                          (int64_t)(key & (ps - 1)) * row_bytes + (kv ? (int64_t)v_off * 2 : 0);
+          dma16_flat(p + src, (kv ? mv : mk) + 1024u * j);
+        }
     }
   };
-  // WAVE_PAGE byte offsets inside a page: key k0 + tk + i sits at slot
-  // (k0 - page start) + tk + i, clamped to the slot of the row's last key; the
-  // per-thread part is fixed, the rest is uniform.
-  const int tk = kg * KPT - 16 * wave;  // this thread's first key within the wave's 16
-  uint32_t toff[KPT];
+
+  // S^T (32 keys x 16 queries per block) of the step in buffer buf.
+  // sacc[b][kb][r] is key 16 kb + 4 lg + r of the step, query li of block b.
+  auto qk = [&](int buf, f32x4_t (&sacc)[NQB][2]) {
+    const uint8_t* kp = sK + buf * BUFB + li * ROWB;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) toff[i] = (uint32_t)(tk + i) * row_bytes + seg * 16u;
-  u32x4_t gk[KPT], gv[KPT];
-  // Global loads of tile t into registers: K (kv = 0) into gk, V (kv = 1) into gv.
-  auto gload = [&](int t, const int (&pid)[KPT], int kv, u32x4_t (&dst)[KPT]) {
-    if constexpr (DENSE) {
-      // key k0 + tk + i of the row at byte (k0 + tk + i) * row_bytes, clamped to
-      // the row's last key
-      const char* base_p = reinterpret_cast<const char*>(kv ? a.v_dense : a.k_dense) +
-                           (int64_t)page_base * row_bytes + head_bytes;
-      const int k0 = wave_key0(t);
-      const uint32_t base = (uint32_t)k0 * row_bytes;
-      const uint32_t lim = (uint32_t)(kv_len - 1) * row_bytes + seg * 16u;
+    for (int b = 0; b < NQB; ++b) {
+      sacc[b][0] = f32x4_t{};
+      sacc[b][1] = f32x4_t{};
+    }
 #pragma unroll
-      for (int i = 0; i < KPT; ++i)
-        dst[i] = *reinterpret_cast<const u32x4_t*>(base_p + min(base + toff[i], lim));
-    } else if constexpr (WAVE_PAGE) {
-      const char* base_p = reinterpret_cast<const char*>(a.cache) +
-                           (int64_t)pid[0] * page_elems * 2 + head_bytes +
-                           (kv ? (int64_t)v_off * 2 : 0);
-      const int k0 = wave_key0(t);
-      const int pstart = (k0 < kv_len ? k0 : kv_len - 1) & ~(ps - 1);
-      const uint32_t base = (uint32_t)(k0 - pstart) * row_bytes;
-      const uint32_t lim = (uint32_t)(kv_len - 1 - pstart) * row_bytes + seg * 16u;
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int i = 0; i < KPT; ++i)
-        dst[i] = *reinterpret_cast<const u32x4_t*>(base_p + min(base + toff[i], lim));
-    } else {
+      for (int s = 0; s < KSTEPS; ++s) {
+        // logical segment 4 s + lg of row 16 kb + li (kswz(16 kb + li) = kswz(li))
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(
+            kp + kb * 16 * ROWB + 16 * ((4 * s + lg) ^ kswz(li)));
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int key = key_of(t, i);
-        const uint16_t* p = a.cache + (int64_t)pid[i] * page_elems +
-                            (key & (ps - 1)) * row_elems + hk * D + seg * 8 + (kv ? v_off : 0);
-        dst[i] = *reinterpret_cast<const u32x4_t*>(p);
+        for (int b = 0; b < NQB; ++b) sacc[b][kb] = mfma16(kf, qreg[b][s], sacc[b][kb]);
       }
     }
   };
-  auto swrite_k = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      *reinterpret_cast<u32x4_t*>(&sK[buf * KBUF + (kg * KPT + i) * KS + seg * 8]) = gk[i];
-  };
-  auto swrite_v = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i)
-      *reinterpret_cast<u32x4_t*>(&sV[buf * VBUF + (kg * KPT + i) * VS + seg * 8]) = gv[i];
-  };
-
-  // S^T (64 keys x 32 queries) of the tile in buffer buf.
-  // sacc[kb2][r] is key 32 kb2 + 8 (r/4) + 4 half + r%4 of the tile, query jcol.
-  auto qk = [&](int buf, f32x16_t (&sacc)[2]) {
-    const uint16_t* kp = sK + buf * KBUF + jcol * KS + 8 * half;
-    sacc[0] = f32x16_t{};
-    sacc[1] = f32x16_t{};
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kp + kb2 * 32 * KS + 16 * s);
-        sacc[kb2] = mfma32(kf, qreg[s], sacc[kb2]);
-      }
-    }
-  };
-  // Does the tile at kbase cross the causal diagonal, the window edge or the
+  // Does the step at kbase cross the causal diagonal, the window edge or the
   // row end?  (uniform)
   auto needs_mask = [&](int kbase) {
     return (kbase + BN - 1 > (causal ? p_first : kv_len - 1)) || (kbase + BN > kv_len) ||
            (wl >= 0 && kbase < p_last - wl);
   };
   // Scores of keys outside [lo_j, hi_j] become -inf.
-  auto apply_mask = [&](f32x16_t (&sacc)[2], int kbase) {
-    const int k0 = kbase + 4 * half;
+  auto apply_mask = [&](f32x4_t (&sacc)[NQB][2], int kbase) {
+    const int k0 = kbase + 4 * lg;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+    for (int b = 0; b < NQB; ++b) {
+      const int pos = pos_of(b);
+      const int hi_j = causal ? min(pos, kv_len - 1) : kv_len - 1;
+      const int lo_j = wl >= 0 ? pos - wl : 0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * kb2 + 8 * (r >> 2) + (r & 3);
-        sacc[kb2][r] = (key > hi_j || key < lo_j) ? -INFINITY : sacc[kb2][r];
-      }
-  };
-  // Max of the raw scores of this lane's query column (both halves).
-  auto colmax = [&](const f32x16_t (&sacc)[2]) {
-    // Three-input maxima (v_max3_f32): 32 values in 16 instructions.
-    float m3[8];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const f32x16_t& v = sacc[k >> 2];
-      const int r = 4 * (k & 3);
-      m3[k] = fmaxf(fmaxf(v[r], v[r + 1]), fmaxf(v[r + 2], v[r + 3]));
-    }
-    const float a = fmaxf(fmaxf(m3[0], m3[1]), m3[2]);
-    const float b = fmaxf(fmaxf(m3[3], m3[4]), m3[5]);
-    const float mr = fmaxf(fmaxf(m3[6], m3[7]), fmaxf(a, b));
-    return fmaxf(mr, __shfl_xor(mr, 32));
-  };
-  // Move the running max (and rescale O, l) only when some query's new maximum
-  // exceeds it by more than the slack (uniform branch).
-  auto update_max = [&](float mr) {
-    const float mt = mr * c;
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack) != 0) {
-      const float mn = fmaxf(m_run, mt);
-      const float alpha = fast_exp2(m_run - mn);
-      m_run = mn;
-      l_run *= alpha;
-#pragma unroll
-      for (int b = 0; b < DBLK; ++b) oacc[b] *= alpha;
-    }
-  };
-  // P = exp2(S*c - m) as the bf16 P^T operand; step s = 2 kb2 + t holds keys
-  // 16 s + {0..3, 8..11} + 4 half.
-  auto expsum = [&](const f32x16_t (&sacc)[2], u32x4_t (&pb)[4]) {
-    const float neg_m = -m_run;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = fast_exp2(fmaf(sacc[kb2][8 * t + e], c, neg_m));
-          l_run += p[e];  // fp32 P: a sum of the bf16-rounded P misses the LSE bound
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + 16 * kb + r;
+          sacc[b][kb][r] = (key > hi_j || key < lo_j) ? -INFINITY : sacc[b][kb][r];
         }
-        pb[2 * kb2 + t] = u32x4_t{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]),
-                                  cvt_pk_bf16(p[4], p[5]), cvt_pk_bf16(p[6], p[7])};
+    }
+  };
+  // Max of the raw scores of each query column of this lane (all four row groups).
+  auto colmax = [&](const f32x4_t (&sacc)[NQB][2], float (&mr)[NQB]) {
+#pragma unroll
+    for (int b = 0; b < NQB; ++b) {
+      const float x = fmaxf(fmaxf(sacc[b][0][0], sacc[b][0][1]), fmaxf(sacc[b][0][2], sacc[b][0][3]));
+      const float y = fmaxf(fmaxf(sacc[b][1][0], sacc[b][1][1]), fmaxf(sacc[b][1][2], sacc[b][1][3]));
+      mr[b] = max_x32(max_x16(fmaxf(x, y)));
+    }
+  };
+  // Move the running maxima (and rescale O, l) only when some query's new
+  // maximum exceeds its running max by more than the slack (uniform branch).
+  auto update_max = [&](const float (&mr)[NQB]) {
+    bool need = false;
+#pragma unroll
+    for (int b = 0; b < NQB; ++b) need |= mr[b] * c > m_run[b] + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int b = 0; b < NQB; ++b) {
+        const float mn = fmaxf(m_run[b], mr[b] * c);
+        const float alpha = fast_exp2(m_run[b] - mn);
+        m_run[b] = mn;
+        l_run[b] *= alpha;
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d) oacc[b][d] *= alpha;
       }
     }
   };
-  // O^T += V^T . P^T for the tile in buffer buf; the transposed reads deliver
-  // column 32 b + jcol at the keys of pb[s].
-  const int grp = lane >> 4, ga = lane & 15;
-  const int v_lane = (4 * (grp >> 1) + (ga >> 2)) * VS + 16 * (grp & 1) + 4 * (ga & 3);
-  auto pv = [&](int buf, const u32x4_t (&pb)[4]) {
-    const uint16_t* vb = sV + buf * VBUF + v_lane;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int b = 0; b < DBLK; ++b) {
-        const uint16_t* vp = vb + 16 * s * VS + 32 * b;
-        const u32x2_t v0 = lds_read_tr16(vp);
-        const u32x2_t v1 = lds_read_tr16(vp + 8 * VS);
-        oacc[b] = mfma32(u32x4_t{v0[0], v0[1], v1[0], v1[1]}, pb[s], oacc[b]);
-      }
-    }
-  };
-
+  // Lane (li, lg) points at row 4 lg + li/4 (and 16 more), columns
+  // 16 db + 4 (li % 4) .. +3: logical segment 2 db + (li % 4) / 2, half li % 2.
+  const int v_row = 4 * lg + (li >> 2);
+  const int v_z = vswz(v_row);  // equal for v_row + 16
+  const int v_h = ((li & 3) >> 1) * 16 + (li & 1) * 8;
   // ---- pipeline ----
-  // K runs two tiles ahead of the softmax and V one: at step i the registers
-  // hold K(i+2) and V(i+1), which go to the K buffer of tile i (last read by
-  // the scores of tile i in step i-1) and the V buffer of tile i-1 (last read
-  // by step i-1's O update).  So one barrier per step separates every LDS
-  // write from the reads before and after it.
-  int pid_k[KPT], pid_v[KPT];
-  {
-    int pid0[KPT];
-    load_pids(0, pid0);
-    load_pids(1, pid_k);
-    gload(0, pid0, 0, gk);
-    gload(0, pid0, 1, gv);
-  }
-  swrite_k(0);
-  swrite_v(0);
-  gload(1, pid_k, 0, gk);
-  load_pids(2, pid_k);
-  load_pids(1, pid_v);
-  swrite_k(1);
-  gload(2, pid_k, 0, gk);
-  gload(1, pid_v, 1, gv);
-  load_pids(3, pid_k);
-  load_pids(2, pid_v);
+  // Step t's K and V are copied PF steps ahead, into buffer t % NBUF.  Step i
+  // reads K(i+1) and V(i) and issues the copies of step i+PF, into the buffer
+  // of step i-1, whose last reads (K in step i-2, V in step i-1) precede the
+  // barrier that ends step i-1.  Before that barrier every wave waits for its
+  // copies of step i+1 (copies land in issue order), leaving PF-2 steps of
+  // copies in flight.
+  constexpr int NL = 2 * NI;  // copies per wave per step
+#pragma unroll
+  for (int t = 0; t < PF; ++t) issue(t, t);
+  wait_copies<(PF - 1) * NL>();
   __syncthreads();
-  f32x16_t sa[2], sb[2];
-  qk(0, sa);
-  if (needs_mask(kstart)) apply_mask(sa, kstart);
-  update_max(colmax(sa));
-  __syncthreads();  // step 0 overwrites the K buffer just read
+  f32x4_t sa[NQB][2], sb[NQB][2];
+  {
+    qk(0, sa);
+    if (needs_mask(kstart)) apply_mask(sa, kstart);
+    float mr[NQB];
+    colmax(sa, mr);
+    update_max(mr);
+  }
+  wait_copies<(PF - 2) * NL>();
+  __syncthreads();
 
-  // One step: softmax and O update for tile i (scores in cur), scores of tile
-  // i+1 into nxt.  Past the last tile the clamped loads repeat it; those
-  // scores are never used.
-  auto step = [&](f32x16_t (&cur)[2], f32x16_t (&nxt)[2], int i) {
-    const int buf = i & 1;
-    u32x4_t pb[4];
-    // S of the next tile on the matrix cores while the VALU turns the current
-    // scores into P.
-    qk(buf ^ 1, nxt);
-    expsum(cur, pb);
-    // LDS reads run kAhead fragments ahead of the MFMA that consumes them.
-    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+  // One step: softmax and O update for step i (scores in cur), scores of step
+  // i+1 into nxt.  Past the last step the clamped copies repeat it; those
+  // scores are never used.  The instruction order is written out: LDS
+  // fragments are read KA groups ahead of the MFMAs that use them, and
+  // scheduling fences keep that order.
+  constexpr int NG = 2 * KSTEPS;         // K fragments per step (16 keys x 32 d)
+  constexpr int NEA = 8 * NQB;           // exponentials per lane per step
+  constexpr int KA = PKV_PREFILL_KA;     // fragment groups read ahead
+  // bi = i % NBUF, carried from step to step (no division).
+  auto step = [&](f32x4_t (&cur)[NQB][2], f32x4_t (&nxt)[NQB][2], int i, int bi) {
+    const int bn = bi + 1 == NBUF ? 0 : bi + 1;   // (i + 1) % NBUF
+    const int bp = bi == 0 ? NBUF - 1 : bi - 1;   // (i + PF) % NBUF = (i - 1) % NBUF
+    issue(i + PF, bp);
+    u32x4_t pb[NQB];
+    // ---- S(i+1) on the matrix cores while the VALU turns S(i) into P ----
+    {
+      const uint8_t* kp = sK + bn * BUFB + li * ROWB;
+      // fragment g: keys 16 (g / KSTEPS) + li, logical segment 4 (g % KSTEPS) + lg
+      auto kread = [&](int gi) {
+        return *reinterpret_cast<const u32x4_t*>(
+            kp + (gi / KSTEPS) * 16 * ROWB + 16 * ((4 * (gi % KSTEPS) + lg) ^ kswz(li)));
+      };
+      u32x4_t kf[KA + 1];
 #pragma unroll
-    for (int k = 0; k < 2 * KSTEPS; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      if (k + kAhead < 2 * KSTEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuQK, 0);  // VALU
+      for (int gi = 0; gi < KA; ++gi) kf[gi] = kread(gi);
+      float pe[NQB][2][4];
+      // exponential e of the lane's 8 * NQB: block (e / 4) % NQB, key block
+      // e / (4 NQB), element e % 4
+      auto expo = [&](int e) {
+        const int b = (e / 4) % NQB, kb = e / (4 * NQB), r = e % 4;
+        const float p = fast_exp2(fmaf(cur[b][kb][r], c, -m_run[b]));
+        pe[b][kb][r] = p;
+        l_run[b] += p;  // fp32 P: a sum of the bf16-rounded P misses the LSE bound
+        if (r & 1) pb[b][2 * kb + r / 2] = cvt_pk_bf16(pe[b][kb][r - 1], p);
+      };
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        if (gi + KA < NG) kf[(gi + KA) % (KA + 1)] = kread(gi + KA);
+        const int kb = gi / KSTEPS, st = gi % KSTEPS;
+#pragma unroll
+        for (int b = 0; b < NQB; ++b) {
+          nxt[b][kb] = mfma16(kf[gi % (KA + 1)], qreg[b][st], st == 0 ? f32x4_t{} : nxt[b][kb]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // P of step i.  On the VALU, after the matrix work above is issued: the
+      // other wave on the SIMD (another workgroup, at another phase) keeps
+      // the matrix cores busy meanwhile.
+#pragma unroll
+      for (int e = 0; e < NEA; ++e) expo(e);
     }
-    // Pin P here: without a use the compiler would sink its computation past
-    // the masking branch below, out of reach of the matrix-core work above.
-#pragma unroll
-    for (int k = 0; k < 4; ++k) asm volatile("" ::"v"(pb[k]));
-    // Stage K(i+2) and V(i+1); issue the loads of K(i+3) and V(i+2).
-    swrite_k(buf);
-    swrite_v(buf ^ 1);
-    gload(i + 3, pid_k, 0, gk);
-    gload(i + 2, pid_v, 1, gv);
-    load_pids(i + 4, pid_k);
-    load_pids(i + 3, pid_v);
     const int knext = kstart + (i + 1) * BN;
     if (needs_mask(knext)) apply_mask(nxt, knext);
-    // O += P V for the current tile on the matrix cores while the VALU finds
-    // the next tile's column maxima.
-    pv(buf, pb);
-    const float mr = colmax(nxt);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 1);
+    // ---- O += P V on the matrix cores while the VALU finds S(i+1)'s maxima ----
+    float mr[NQB];
+    {
+      const uint8_t* vb = sV + bi * BUFB + v_row * ROWB + v_h;
+      auto vread = [&](int db) {
+        const uint8_t* vp = vb + 16 * ((2 * db) ^ v_z);
+        const u32x2_t v0 = lds_read_tr16(reinterpret_cast<const uint16_t*>(vp));
+        const u32x2_t v1 = lds_read_tr16(reinterpret_cast<const uint16_t*>(vp + 16 * ROWB));
+        return u32x4_t{v0[0], v0[1], v1[0], v1[1]};
+      };
+      u32x4_t vf[KA + 1];
 #pragma unroll
-    for (int k = 0; k < 4 * DBLK; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      if (k + kAhead < 4 * DBLK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // two DS reads
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuPV, 1);  // VALU
+      for (int db = 0; db < KA; ++db) vf[db] = vread(db);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        if (db + KA < DBLK) vf[(db + KA) % (KA + 1)] = vread(db + KA);
+#pragma unroll
+        for (int b = 0; b < NQB; ++b) {
+          const int k = db * NQB + b;
+          oacc[b][db] = mfma16(vf[db % (KA + 1)], pb[b], oacc[b][db]);
+          // column maxima of S(i+1) in the first 3 NQB slots: per block the
+          // lane's 8 keys, then the exchanges with lanes ^ 16 and ^ 32
+          if (k < NQB) {
+            const float x = fmaxf(fmaxf(nxt[k][0][0], nxt[k][0][1]), fmaxf(nxt[k][0][2], nxt[k][0][3]));
+            const float y = fmaxf(fmaxf(nxt[k][1][0], nxt[k][1][1]), fmaxf(nxt[k][1][2], nxt[k][1][3]));
+            mr[k] = fmaxf(x, y);
+          } else if (k < 2 * NQB) {
+            mr[k - NQB] = max_x16(mr[k - NQB]);
+          } else if (k < 3 * NQB) {
+            mr[k - 2 * NQB] = max_x32(mr[k - 2 * NQB]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
     update_max(mr);
+    wait_copies<(PF - 2) * NL>();
     __syncthreads();
   };
 
-  int i = 0;
+  int i = 0, bi = 0;
   for (; i + 1 < ntiles; i += 2) {
-    step(sa, sb, i);
-    step(sb, sa, i + 1);
+    step(sa, sb, i, bi);
+    bi = bi + 1 == NBUF ? 0 : bi + 1;
+    step(sb, sa, i + 1, bi);
+    bi = bi + 1 == NBUF ? 0 : bi + 1;
   }
-  if (i < ntiles) step(sa, sb, i);
+  if (i < ntiles) step(sa, sb, i, bi);
+  // Copies of the clamped steps past the end may still be in flight: let them
+  // land before the workgroup ends and its LDS goes to another.
+  wait_copies<0>();
 
   // ---- normalise and store ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qvalid) {
-    const float inv = 1.f / l_tot;
-    uint16_t* op = a.out + ((int64_t)token * Hq + qh) * D;
 #pragma unroll
-    for (int b = 0; b < DBLK; ++b) {
+  for (int b = 0; b < NQB; ++b) {
+    const float l_tot = sum_x32(sum_x16(l_run[b]));
+    int qh, tl;
+    pair_of(b, qh, tl);
+    const int64_t qi = (int64_t)(q_base + q_start + tl) * Hq + qh;
+    if (tl < q_count) {
+      const float inv = 1.f / l_tot;
+      uint16_t* op = a.out + qi * D + 4 * lg;
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d0 = 32 * b + 8 * rq + 4 * half;
-        u32x2_t w2 = {cvt_pk_bf16(oacc[b][4 * rq + 0] * inv, oacc[b][4 * rq + 1] * inv),
-                      cvt_pk_bf16(oacc[b][4 * rq + 2] * inv, oacc[b][4 * rq + 3] * inv)};
-        *reinterpret_cast<u32x2_t*>(op + d0) = w2;
+      for (int db = 0; db < DBLK; ++db) {
+        u32x2_t w2 = {cvt_pk_bf16(oacc[b][db][0] * inv, oacc[b][db][1] * inv),
+                      cvt_pk_bf16(oacc[b][db][2] * inv, oacc[b][db][3] * inv)};
+        *reinterpret_cast<u32x2_t*>(op + 16 * db) = w2;
       }
+      if (a.lse != nullptr && lg == 0)
+        a.lse[qi] = (m_run[b] + log2f(l_tot)) * kLn2;
     }
-    if (a.lse != nullptr && half == 0)
-      a.lse[(int64_t)token * Hq + qh] = (m_run + log2f(l_tot)) * kLn2;
   }
 }
 
