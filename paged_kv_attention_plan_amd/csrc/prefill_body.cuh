@@ -350,25 +350,30 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
         }
     }
   };
-  // Max of the raw scores of each query column of this lane (all four row groups).
-  auto colmax = [&](const f32x4_t (&sacc)[NQB][2], float (&mr)[NQB]) {
+  // Max of the raw scores of each query block held by this lane (its 8 keys
+  // of the step; the other three row groups hold the rest of the column).
+  auto lanemax = [&](const f32x4_t (&sacc)[NQB][2], float (&lm)[NQB]) {
 #pragma unroll
     for (int b = 0; b < NQB; ++b) {
       const float x = fmaxf(fmaxf(sacc[b][0][0], sacc[b][0][1]), fmaxf(sacc[b][0][2], sacc[b][0][3]));
       const float y = fmaxf(fmaxf(sacc[b][1][0], sacc[b][1][1]), fmaxf(sacc[b][1][2], sacc[b][1][3]));
-      mr[b] = max_x32(max_x16(fmaxf(x, y)));
+      lm[b] = fmaxf(x, y);
     }
   };
-  // Move the running maxima (and rescale O, l) only when some query's new
-  // maximum exceeds its running max by more than the slack (uniform branch).
-  auto update_max = [&](const float (&mr)[NQB]) {
+  // Move the running maxima (and rescale O, l) only when some score exceeds
+  // its query's running max by more than the slack.  Each lane tests its own
+  // scores, so the column maxima across the four row groups (two exchanges
+  // per block) are formed only on that rare branch (uniform over the wave);
+  // there every query's max moves to its column max, which is always exact.
+  auto update_max = [&](const float (&lm)[NQB]) {
     bool need = false;
 #pragma unroll
-    for (int b = 0; b < NQB; ++b) need |= mr[b] * c > m_run[b] + kRescaleSlack;
+    for (int b = 0; b < NQB; ++b) need |= lm[b] * c > m_run[b] + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
       for (int b = 0; b < NQB; ++b) {
-        const float mn = fmaxf(m_run[b], mr[b] * c);
+        const float mr = max_x32(max_x16(lm[b]));
+        const float mn = fmaxf(m_run[b], mr * c);
         const float alpha = fast_exp2(m_run[b] - mn);
         m_run[b] = mn;
         l_run[b] *= alpha;
@@ -398,9 +403,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
   {
     qk(0, sa);
     if (needs_mask(kstart)) apply_mask(sa, kstart);
-    float mr[NQB];
-    colmax(sa, mr);
-    update_max(mr);
+    float lm[NQB];
+    lanemax(sa, lm);
+    update_max(lm);
   }
   wait_copies<(PF - 2) * NL>();
   __syncthreads();
@@ -459,7 +464,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
     const int knext = kstart + (i + 1) * BN;
     if (needs_mask(knext)) apply_mask(nxt, knext);
     // ---- O += P V on the matrix cores while the VALU finds S(i+1)'s maxima ----
-    float mr[NQB];
+    float lm[NQB];
     {
       const uint8_t* vb = sV + bi * BUFB + v_row * ROWB + v_h;
       auto vread = [&](int db) {
@@ -478,22 +483,17 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
         for (int b = 0; b < NQB; ++b) {
           const int k = db * NQB + b;
           oacc[b][db] = mfma16(vf[db % (KA + 1)], pb[b], oacc[b][db]);
-          // column maxima of S(i+1) in the first 3 NQB slots: per block the
-          // lane's 8 keys, then the exchanges with lanes ^ 16 and ^ 32
+          // the lane's maxima of S(i+1) in the first NQB slots
           if (k < NQB) {
             const float x = fmaxf(fmaxf(nxt[k][0][0], nxt[k][0][1]), fmaxf(nxt[k][0][2], nxt[k][0][3]));
             const float y = fmaxf(fmaxf(nxt[k][1][0], nxt[k][1][1]), fmaxf(nxt[k][1][2], nxt[k][1][3]));
-            mr[k] = fmaxf(x, y);
-          } else if (k < 2 * NQB) {
-            mr[k - NQB] = max_x16(mr[k - NQB]);
-          } else if (k < 3 * NQB) {
-            mr[k - 2 * NQB] = max_x32(mr[k - 2 * NQB]);
+            lm[k] = fmaxf(x, y);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
-    update_max(mr);
+    update_max(lm);
     wait_copies<(PF - 2) * NL>();
     __syncthreads();
   };
