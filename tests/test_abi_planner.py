@@ -117,7 +117,7 @@ def test_decode_workers_are_balanced(seed, hq, hk, num_cus, wpc):
 
 @pytest.mark.parametrize("causal,window_left,hq,hk,ps", [
     (True, -1, 8, 2, 4), (True, 6, 4, 4, 16), (False, -1, 8, 1, 1), (False, 9, 2, 1, 8),
-    (True, -1, 16, 2, 64)])
+    (True, -1, 16, 2, 64), (True, -1, 6, 2, 16), (True, 7, 24, 2, 8)])
 def test_prefill_plan_matches_policy(causal, window_left, hq, hk, ps):
     w = synth.random_case(50, kind="prefill", batch=6, num_qo_heads=hq, num_kv_heads=hk,
                           head_dim=64, page_size=ps, max_kv=200, causal=causal,
@@ -204,6 +204,20 @@ def _err(fn):
     with pytest.raises(pkv.PkvError) as ei:
         fn()
     return ei.value.status
+
+
+def test_error_prefill_group_must_divide_tile_pairs():
+    """Prefill tiles hold 192 (query head, token) pairs, so the GQA group
+    num_qo_heads / num_kv_heads must divide 192: 3 and 64 do, 128 does not."""
+    for hq, hk, ok in ((6, 2, True), (64, 1, True), (128, 1, False), (5, 1, False)):
+        w = synth.random_case(51, kind="prefill", batch=2, num_qo_heads=hq, num_kv_heads=hk,
+                              head_dim=64, page_size=16, max_kv=40)
+        mk = lambda: pkv.plan_create(_params(w, "prefill"), w.qo_indptr, w.kv_indptr,
+                                     w.kv_indices, w.last_page_len)
+        if ok:
+            mk()
+        else:
+            assert _err(mk) == pkv.E_UNSUPPORTED
 
 
 def test_errors_unsupported_head_dim_and_page_size():

@@ -90,6 +90,11 @@ PREFILL = [
     (204, 128, 4, 2, 64, False, 40, "nan"),
     (205, 64, 8, 8, 4, True, 0, "zero"),
     (206, 128, 16, 16, 16, True, 300, "nan"),
+    # group sizes whose query blocks straddle heads inside a 16-lane block
+    (207, 128, 6, 2, 16, True, -1, "nan"),     # g 3: 64 tokens per tile
+    (208, 128, 32, 2, 16, True, 100, "nan"),   # g 16: 12 tokens per tile
+    (209, 64, 24, 2, 8, True, -1, "nan"),      # g 12, pages of 8 (per-lane page ids)
+    (210, 128, 64, 1, 32, False, -1, "nan"),   # g 64: 3 tokens per tile
 ]
 
 
