@@ -617,7 +617,7 @@ def main():
         for name in ("long_decode", "ragged_prefill", "mixed_window", "gqa_decode_context_only",
                      "ragged_prefill_dense", "tiny_decode_graph"):
             if name != args.config:
-                sec.append(secondary(name, dev, max(5, args.steps // 5), 2))
+                sec.append(secondary(name, dev, max(5, args.steps // 5), 5))
         line["secondary"] = sec
     if not args.no_ceilings:
         line["measured_ceilings"] = ceilings(dev)
