@@ -425,6 +425,7 @@ def probe_ceilings(dev):
         return {"probes": "libpkv_ceilings.so not built"}
     lib = ctypes.CDLL(path)
     lib.pkv_ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.pkv_ceiling_mfma16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.pkv_ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                      ctypes.c_int, ctypes.c_void_p]
     stream = torch.cuda.current_stream(dev)
@@ -447,6 +448,9 @@ def probe_ceilings(dev):
     ms = best_ms(lambda: lib.pkv_ceiling_mfma(ctypes.c_void_p(sink.data_ptr()), blocks, iters, sh),
                  warm=3)
     mfma_tfs = blocks * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
+    ms = best_ms(lambda: lib.pkv_ceiling_mfma16(ctypes.c_void_p(sink.data_ptr()), blocks, iters, sh),
+                 warm=3)
+    mfma16_tfs = blocks * 4 * iters * 8 * 16384 / (ms * 1e-3) / 1e12
     nbytes = 2 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
     ms = best_ms(lambda: lib.pkv_ceiling_read(ctypes.c_void_p(src.data_ptr()), nbytes,
@@ -456,6 +460,9 @@ def probe_ceilings(dev):
     torch.cuda.empty_cache()
     return {"mfma_loop_TFLOPs": round(mfma_tfs, 1), "read_GBps": round(read_gbs, 1),
             "mfma_loop": "register-only v_mfma_f32_32x32x16_bf16 loop, 16384 waves, best of 5",
+            "mfma16_loop_TFLOPs": round(mfma16_tfs, 1),
+            "mfma16_loop": "the same with v_mfma_f32_16x16x32_bf16 (the prefill kernel's shape), "
+                           "8 chains per wave, best of 5",
             "read": "streaming read of 2 GiB, 512 x 256 threads, 4 x 16-byte loads in flight, best of 5"}
 
 

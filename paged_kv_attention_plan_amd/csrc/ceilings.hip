@@ -37,6 +37,29 @@ __global__ __launch_bounds__(256, 2) void mfma_loop_kernel(float* out, int iters
   out[(size_t)blockIdx.x * blockDim.x + t] = s;
 }
 
+// The same with v_mfma_f32_16x16x32_bf16 (16384 FLOP each), the shape of the
+// prefill kernel: eight independent chains per wave.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256, 2) void mfma16_loop_kernel(float* out, int iters) {
+  const uint32_t t = threadIdx.x;
+  u32x4_t ai = {t * 2654435761u, t ^ 0x3f800000u, t + 7u, t * 97u};
+  u32x4_t bi = {t + 1u, t * 3u, t ^ 0x40000000u, t * 13u};
+  ai &= 0x3fff3fffu;
+  bi &= 0x3fff3fffu;
+  const bf16x8_t a = __builtin_bit_cast(bf16x8_t, ai);
+  const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bi);
+  f32x4_t c[8] = {};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      c[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16((k & 1) ? a : b, (k & 2) ? a : b, c[k], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s += c[k][0] + c[k][1] + c[k][2] + c[k][3];
+  out[(size_t)blockIdx.x * blockDim.x + t] = s;
+}
+
 // Grid-stride read of n_vec 16-byte vectors (non-temporal: each byte once),
 // four loads in flight per thread, folded into one word per thread.
 __global__ __launch_bounds__(256) void read_kernel(const u32x4_t* src, int64_t n_vec,
@@ -63,6 +86,14 @@ extern "C" {
 int pkv_ceiling_mfma(float* out, int blocks, int iters, void* stream) {
   if (out == nullptr || blocks < 1 || iters < 1) return 1;
   hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), out, iters);
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+// out: device float[blocks * 256].  FLOPs = blocks * 4 waves * iters * 8 * 16384.
+int pkv_ceiling_mfma16(float* out, int blocks, int iters, void* stream) {
+  if (out == nullptr || blocks < 1 || iters < 1) return 1;
+  hipLaunchKernelGGL(mfma16_loop_kernel, dim3(blocks), dim3(256), 0,
                      static_cast<hipStream_t>(stream), out, iters);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
