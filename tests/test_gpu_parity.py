@@ -110,6 +110,35 @@ def test_prefill_small(pkv, gpu, case):
     compare(out, lse, ref_o, ref_l, f"prefill s{seed}")
 
 
+def _random_prefill_shapes(n=16, seed=4242):
+    """Seeded prefill shapes across head dims, GQA groups (including ones that
+    straddle heads inside a 16-lane query block), page sizes, masks and stale data."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        D = int(rng.choice([64, 128]))
+        g = int(rng.choice([1, 2, 3, 4, 6, 8, 16]))
+        hk = int(rng.choice([1, 2, 4])) if g <= 8 else 1
+        ps = int(rng.choice([1, 2, 8, 16, 32, 64, 128]))
+        causal = bool(rng.integers(0, 2))
+        wl = int(rng.choice([-1, -1, 0, 17, 130]))
+        out.append((300 + k, D, g * hk, hk, ps, causal, wl, "nan" if k % 2 else "zero"))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_prefill_shapes(),
+                         ids=lambda c: f"s{c[0]}-D{c[1]}-g{c[2]//c[3]}-ps{c[4]}-c{int(c[5])}-w{c[6]}")
+def test_prefill_random_shapes(pkv, gpu, case):
+    seed, D, hq, hk, ps, causal, wl, stale = case
+    say(f"case prefill sweep seed={seed} D={D} Hq={hq} Hk={hk} ps={ps} causal={causal} window={wl}")
+    w = synth.random_case(seed, kind="prefill", batch=5, num_qo_heads=hq, num_kv_heads=hk,
+                          head_dim=D, page_size=ps, max_kv=400, causal=causal, window_left=wl,
+                          stale=stale, device=gpu)
+    out, lse, plan, _ = gpu_run(pkv, w)
+    ref_o, ref_l = _full_oracle(w)
+    compare(out, lse, ref_o, ref_l, f"prefill sweep s{seed}")
+
+
 def test_mixed_small(pkv, gpu):
     say("case mixed_window cut to 12 decode rows + 4 prompt rows")
     w = synth.make_workload("mixed_window", scale_rows=12, device=gpu, stale="nan")
