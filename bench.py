@@ -27,6 +27,8 @@ Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import contextlib
+import gc
 import json
 import os
 import sys
@@ -308,15 +310,16 @@ class Runner:
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(steps):
-            self.step()
-        e1.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+        with no_gc_pause():
+            t0 = time.perf_counter()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                self.step()
+            e1.record()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
 
     def kernel_times(self, steps):
@@ -502,6 +505,21 @@ def cpu_baseline(runner, unit, budget_s=12.0):
     return {"value": round(value, 6), "unit": unit, "cores": int(cores), "kind": "oracle",
             "sample": f"first {done} of {w.batch} requests of the same seeded input, every query "
                       f"head (float64 numpy), {elapsed:.1f} s"}
+
+
+@contextlib.contextmanager
+def no_gc_pause():
+    """Python's cycle collector off inside a timed loop: a full collection over
+    the many objects alive by the later workloads takes tens of milliseconds,
+    during which the host issues nothing and the GPU idles.  (Nothing is
+    collected here: that would change which memory later workloads reuse.)"""
+    was = gc.isenabled()
+    gc.disable()
+    try:
+        yield
+    finally:
+        if was:
+            gc.enable()
 
 
 def secondary(name, dev, steps, warmup):

@@ -92,17 +92,16 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 #endif
 
 // One 16-byte-per-lane copy from memory straight into LDS: lane l's 16 bytes
-// at sbase + voff go to LDS byte m0 + 16 l (global_load_lds_dwordx4).  The
-// compiler does not see these copies; their completion is awaited with
-// wait_copies (vmcnt counts them with the wave's other vector memory reads,
-// which return in issue order).
+// at sbase + voff go to LDS byte m0 + 16 l (global_load_lds_dwordx4; the LDS
+// base is bound to m0 as an operand, so the compiler sets m0 and knows it).
+// The compiler does not see these copies as memory accesses; their completion
+// is awaited with wait_copies (vmcnt counts them with the wave's other vector
+// memory reads, which return in issue order).
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               ::"v"(voff), "s"(sbase), "s"(m0) : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
 }
 __device__ __forceinline__ void dma16_flat(const void* p, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               ::"v"(p), "s"(m0) : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(p), "{m0}"(m0) : "memory");
 }
 // Wait until at most N of this wave's vector memory reads are outstanding.
 template <int N>
