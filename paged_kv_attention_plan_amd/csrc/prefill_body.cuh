@@ -413,7 +413,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
   // i+1 into nxt.  Past the last step the clamped copies repeat it; those
   // scores are never used.  The instruction order is written out: LDS
   // fragments are read KA groups ahead of the MFMAs that use them, and
-  // scheduling fences keep that order.
+  // scheduling fences keep that order for the score MFMAs (the output
+  // update, with the lane maxima between its MFMAs, is left to the compiler's
+  // scheduler: about 1 % faster than fenced).
   constexpr int NG = 2 * KSTEPS;         // K fragments per step (16 keys x 32 d)
   constexpr int NEA = 8 * NQB;           // exponentials per lane per step
   constexpr int KA = PKV_PREFILL_KA;     // fragment groups read ahead
@@ -488,7 +490,6 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
             const float y = fmaxf(fmaxf(nxt[k][1][0], nxt[k][1][1]), fmaxf(nxt[k][1][2], nxt[k][1][3]));
             lm[k] = fmaxf(x, y);
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
