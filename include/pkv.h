@@ -234,8 +234,16 @@ pkv_status pkv_plan_metadata(const pkv_plan* plan, void* dst, size_t bytes);
  * kernel that last read it has flagged its reads done (a flag in the same
  * host-coherent buffer), so re-planning while earlier steps are in flight is safe
  * (attn.dense force_double_buffer hazard); this call waits for that, up to 60 s,
- * then returns PKV_E_DEVICE.  PKV_E_WORKSPACE if workspace_bytes is too small. */
+ * then returns PKV_E_DEVICE.  A plan whose metadata outgrows the staging buffer
+ * re-allocates it (page-locked memory, freed with hipHostFree, which waits for the
+ * device).  PKV_E_WORKSPACE if workspace_bytes is too small. */
 pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Counters of the plan's staging ring (kv.plan PinnedIndexRing: a buffer is reused
+ * only after its last reader is done).  stats[0] = uploads launched, stats[1] =
+ * uploads that found their staging buffer still being read and waited, stats[2] =
+ * nanoseconds spent in those waits.  Host only; PKV_E_INVALID on NULL. */
+pkv_status pkv_plan_upload_stats(const pkv_plan* plan, int64_t stats[3]);
 
 /* Attention for every planned query (FlashInfer*Wrapper.run analogue).
  * q, kv_cache_layer, out: device pointers (layouts above); lse may be NULL.

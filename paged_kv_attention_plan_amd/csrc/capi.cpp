@@ -13,6 +13,7 @@
 #include "kernels.h"
 #include "pkv.h"
 #include "plan.h"
+#include "stage.h"
 
 namespace {
 
@@ -30,46 +31,10 @@ pkv_status fail(pkv_status s, std::string msg) {
       return fail(PKV_E_DEVICE, std::string(#expr) + " failed: " + hipGetErrorString(e_)); \
   } while (0)
 
-// One page-locked, host-coherent buffer of the staging ring (kv.plan
-// PinnedIndexRing): [0, cap) holds the serialised plan, followed by one
-// completion flag per upload workgroup.  Each workgroup of the upload kernel
-// that reads the buffer stores the upload's sequence number into its flag when
-// its reads are done, and the buffer is rewritten only after every flag holds
-// it.  (An event recorded behind the kernel would do the same, but costs the
-// stream a marker packet and several microseconds between kernels.)
 constexpr int kUploadBlocks = 256;  // most workgroups one upload launches
-struct Stage {
-  void* host = nullptr;
-  void* dev = nullptr;  // the same memory as seen by the GPU
-  size_t cap = 0;
-  uint32_t seq = 0;     // sequence number of the last upload from this buffer
-  int n_flags = 0;      // workgroups of that upload
-  bool pending = false;
-  volatile uint32_t* flags() const {
-    return reinterpret_cast<volatile uint32_t*>(static_cast<char*>(host) + cap);
-  }
-};
-
-// Wait until every workgroup of the stage's last upload has finished reading
-// it.  Spins (yielding) for up to 60 s; the GPU then counts as failed.
-bool wait_stage(Stage& s) {
-  if (!s.pending) return true;
-  const auto t0 = std::chrono::steady_clock::now();
-  for (int spin = 0;; ++spin) {
-    int i = 0;
-    while (i < s.n_flags && s.flags()[i] == s.seq) ++i;
-    if (i == s.n_flags) {
-      s.pending = false;
-      return true;
-    }
-    if (spin >= 64) {
-      std::this_thread::yield();
-      if ((spin & 1023) == 0 &&
-          std::chrono::steady_clock::now() - t0 > std::chrono::seconds(60))
-        return false;
-    }
-  }
-}
+// A staging buffer whose readers have not finished after this long counts as
+// a failed GPU.
+constexpr std::chrono::seconds kStageTimeout(60);
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -85,8 +50,7 @@ struct Timing {
 
 struct pkv_plan {
   pkv::PlanData d;
-  Stage stage[2];
-  int next = 0;
+  pkv::StageRing ring;  // page-locked, host-coherent staging buffers of the uploads
   void* uploaded_ws = nullptr;
   mutable Timing timing;
 };
@@ -197,9 +161,9 @@ pkv_status pkv_plan_update(pkv_plan* plan, int32_t batch, const int32_t* qo_indp
 void pkv_plan_destroy(pkv_plan* plan) {
   if (plan == nullptr) return;
   for (hipEvent_t e : plan->timing.pool) (void)hipEventDestroy(e);
-  for (Stage& s : plan->stage) {
+  for (pkv::Stage& s : plan->ring.stage) {
     // A buffer the GPU may still read is not freed (it leaks if the GPU failed).
-    if (s.host != nullptr && wait_stage(s)) (void)hipHostFree(s.host);
+    if (s.host != nullptr && pkv::wait_stage(s, kStageTimeout)) (void)hipHostFree(s.host);
   }
   delete plan;
 }
@@ -274,6 +238,14 @@ pkv_status pkv_plan_info(const pkv_plan* plan, int64_t info[18]) {
   return PKV_OK;
 }
 
+pkv_status pkv_plan_upload_stats(const pkv_plan* plan, int64_t stats[3]) {
+  if (plan == nullptr || stats == nullptr) return fail(PKV_E_INVALID, "NULL argument");
+  stats[0] = plan->ring.uploads;
+  stats[1] = plan->ring.waits;
+  stats[2] = plan->ring.wait_ns;
+  return PKV_OK;
+}
+
 static pkv_status check_paged(const pkv_plan* plan) {
   if (plan != nullptr && plan->d.dense)
     return fail(PKV_E_INVALID, "a dense plan runs through pkv_dense_gather / pkv_dense_run");
@@ -298,9 +270,12 @@ pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_byt
   pkv_status st = check_workspace(plan, workspace, workspace_bytes);
   if (st != PKV_OK) return st;
   const size_t meta = plan->d.ws.meta_bytes;
-  Stage& s = plan->stage[plan->next];
-  if (!wait_stage(s))
+  // The buffer this upload rewrites is free once every workgroup of the
+  // upload that last read it has stored its completion flag.
+  pkv::Stage* sp = plan->ring.acquire(kStageTimeout);
+  if (sp == nullptr)
     return fail(PKV_E_DEVICE, "a staging buffer's upload did not finish within 60 s");
+  pkv::Stage& s = *sp;
   if (s.cap < meta) {
     if (s.host != nullptr) PKV_HIP(hipHostFree(s.host));
     s.host = nullptr;
@@ -322,14 +297,11 @@ pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_byt
   ua.dst = static_cast<uint4*>(workspace);
   ua.n_vec = (int64_t)(meta / 16);  // meta_bytes is a multiple of 256
   ua.flags = reinterpret_cast<uint32_t*>(static_cast<char*>(s.dev) + s.cap);
-  ua.seq = s.seq + 1;
+  ua.seq = plan->ring.next_seq();
   ua.max_blocks = kUploadBlocks;
   int blocks = 0;
   PKV_HIP(pkv::launch_upload(ua, st_, &blocks));
-  s.seq = ua.seq;
-  s.n_flags = blocks;
-  s.pending = true;
-  plan->next ^= 1;
+  plan->ring.launched(blocks);
   plan->uploaded_ws = workspace;
   return PKV_OK;
 }

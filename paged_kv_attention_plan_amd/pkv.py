@@ -76,6 +76,7 @@ def _load():
         "pkv_plan_permutation": (C.c_int, [C.c_void_p, P(C.c_void_p), P(C.c_int32)]),
         "pkv_plan_info": (C.c_int, [C.c_void_p, P(C.c_int64)]),
         "pkv_plan_upload": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+        "pkv_plan_upload_stats": (C.c_int, [C.c_void_p, P(C.c_int64)]),
         "pkv_run": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                               C.c_void_p, C.c_size_t, C.c_void_p]),
         "pkv_append_kv": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -108,7 +109,7 @@ _lib = _load()
 EXPORTED = ("pkv_plan_params_init", "pkv_plan_create", "pkv_plan_update", "pkv_plan_destroy",
             "pkv_plan_decode_tiles", "pkv_plan_prefill_tiles", "pkv_plan_merges",
             "pkv_plan_write_slots", "pkv_plan_permutation", "pkv_plan_info", "pkv_plan_metadata",
-            "pkv_plan_upload",
+            "pkv_plan_upload", "pkv_plan_upload_stats",
             "pkv_run", "pkv_append_kv", "pkv_run_append", "pkv_context_only_views",
             "pkv_dense_plan_create", "pkv_dense_plan_update", "pkv_dense_gather", "pkv_dense_run",
             "pkv_timing_enable", "pkv_timing_read",
@@ -203,6 +204,13 @@ class Plan:
         buf = np.zeros(n, dtype=np.uint8)
         _check(_lib.pkv_plan_metadata(self._h, buf.ctypes.data_as(C.c_void_p), n))
         return buf
+
+    def upload_stats(self) -> dict:
+        """pkv_plan_upload_stats: uploads launched, uploads that waited for their
+        staging buffer's previous reader, and the nanoseconds spent waiting."""
+        v = (C.c_int64 * 3)()
+        _check(_lib.pkv_plan_upload_stats(self._h, v))
+        return {"uploads": int(v[0]), "waits": int(v[1]), "wait_ns": int(v[2])}
 
     def info(self) -> dict:
         v = (C.c_int64 * 18)()

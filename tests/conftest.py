@@ -26,3 +26,13 @@ def gpu():
         pytest.skip("no GPU")
     import torch
     return torch.device("cuda:0")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With PKV_PARITY_LOG set, write every parity comparison's margins there."""
+    path = os.environ.get("PKV_PARITY_LOG")
+    if not path:
+        return
+    mod = sys.modules.get("gpu_common")
+    if mod is not None and mod.PARITY_LOG:
+        mod.write_parity_log(path)

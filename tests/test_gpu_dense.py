@@ -141,4 +141,4 @@ def test_full_ragged_prefill_dense(pkv, gpu):
     ref = oracle_rows(w, rows, tokens=toks)
     for r in rows:
         sel = torch.tensor([int(w.qo_indptr[r]) + t for t in toks[r]], device=gpu)
-        compare(out[sel], lse[sel], ref[r][0], ref[r][1], f"ragged dense row {r}")
+        compare(out[sel], lse[sel], ref[r][0], ref[r][1], f"ragged dense row {r}", flat=True)

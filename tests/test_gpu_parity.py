@@ -1,10 +1,11 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle.
 
-Small cases are compared element by element over every output; the full-size
-workloads are run in the launch configuration the benchmark times and
-compared on sampled rows/tokens.  Tolerances: |out - ref| <= 1e-2 plus half a
-bf16 ulp of ref (the bf16 output's own rounding), max |lse - ref| <= 1e-3;
-write slots and appended bytes bit-exact.
+Every output element is compared with the oracle.  The five full-size
+workloads run in the launch configuration the benchmark times and are held to
+max |out - ref| <= 1e-2 and max |lse - ref| <= 1e-3 on every element.  The
+small edge cases add half a bf16 ulp of ref where |ref| >= 2 (the bf16
+output's own rounding; see gpu_common).  Write slots and appended bytes are
+bit-exact.
 """
 import json
 import os
@@ -15,7 +16,7 @@ import torch
 
 import oracle
 import synth
-from gpu_common import compare, gpu_run, oracle_rows, say
+from gpu_common import compare, gpu_run, oracle_all, oracle_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -213,26 +214,29 @@ def test_repeat_runs_are_deterministic(pkv, gpu):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-# ---- full sizes, sampled ----
-
-def _sample_rows(n, k, seed):
-    rng = np.random.default_rng(seed)
-    return sorted(rng.choice(n, size=min(k, n), replace=False).tolist())
+# ---- full sizes, every element, flat bounds ----
+# Each workload runs in the launch configuration the benchmark times (default
+# plan parameters on the device's CU count), and every output element and LSE
+# is compared with the oracle at max |out - ref| <= 1e-2, max |lse - ref| <= 1e-3.
 
 
 def test_full_gqa_decode_with_append(pkv, gpu):
     say("case gqa_decode full size (128 rows, Hq 32 / Hk 8, D 128, ps 16, 40000-page pool) + append")
     w = synth.make_workload("gqa_decode", device=gpu)
+    before = w.cache.clone()
     out, lse, plan, _ = gpu_run(pkv, w, append=True)
-    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
-    rows = _sample_rows(w.batch, 10, 1) + [int(np.argmax(w.kv_len))]
-    ref = oracle_rows(w, rows)
-    for r in rows:
-        compare(out[r:r + 1], lse[r:r + 1], ref[r][0], ref[r][1], f"gqa_decode row {r} N={w.kv_len[r]}")
-    # the appended token is the last key of each row
-    k_slot = plan.write_slots()
-    page, off = k_slot[rows[0]] // 16, k_slot[rows[0]] % 16
-    assert torch.equal(w.cache[page, 0, off], w.k_new[rows[0]])
+    # the appended tokens, bit for bit, and nothing else of the pool moved
+    slots = oracle.write_slots(16, w.kv_indptr, w.kv_indices, w.last_page_len)
+    assert np.array_equal(plan.write_slots(), slots)
+    sl = torch.from_numpy(slots).to(gpu)
+    page, off = sl // 16, sl % 16
+    assert torch.equal(w.cache[page, 0, off], w.k_new) and torch.equal(w.cache[page, 1, off], w.v_new)
+    before[page, 0, off] = w.k_new
+    before[page, 1, off] = w.v_new
+    assert torch.equal(before.view(torch.int16), w.cache.view(torch.int16))
+    del before
+    ref_o, ref_l = oracle_all(w)
+    compare(out, lse, ref_o, ref_l, "gqa_decode full (all 128 rows)", flat=True)
 
 
 def test_full_long_decode(pkv, gpu):
@@ -240,44 +244,28 @@ def test_full_long_decode(pkv, gpu):
     w = synth.make_workload("long_decode", device=gpu)
     out, lse, plan, _ = gpu_run(pkv, w)
     assert len(plan.merges()) > 0
-    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
-    rows = _sample_rows(w.batch, 3, 2)
-    ref = oracle_rows(w, rows)
-    for r in rows:
-        compare(out[r:r + 1], lse[r:r + 1], ref[r][0], ref[r][1], f"long_decode row {r} N={w.kv_len[r]}")
+    ref_o, ref_l = oracle_all(w)
+    compare(out, lse, ref_o, ref_l, "long_decode full (all 8 rows)", flat=True)
 
 
 def test_full_ragged_prefill(pkv, gpu):
     say("case ragged_prefill full size (16 rows, q 128..2048, prefix 0..4096)")
     w = synth.make_workload("ragged_prefill", device=gpu)
     out, lse, plan, _ = gpu_run(pkv, w)
-    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
-    rows = _sample_rows(w.batch, 4, 3)
-    rng = np.random.default_rng(4)
-    toks = {r: np.unique(np.concatenate([[0, int(w.q_len[r]) - 1],
-                                         rng.integers(0, int(w.q_len[r]), size=40)])) for r in rows}
-    ref = oracle_rows(w, rows, tokens=toks)
-    for r in rows:
-        sel = int(w.qo_indptr[r]) + toks[r]
-        compare(out[sel], lse[sel], ref[r][0], ref[r][1], f"ragged_prefill row {r} L={w.q_len[r]} N={w.kv_len[r]}")
+    ref_o, ref_l = oracle_all(w)
+    compare(out, lse, ref_o, ref_l, f"ragged_prefill full (all {w.total_q} tokens)", flat=True)
 
 
 def test_full_mixed_window(pkv, gpu):
     say("case mixed_window full size (256 decode rows + 4 prompt rows, window 4096)")
     w = synth.make_workload("mixed_window", device=gpu)
     out, lse, plan, _ = gpu_run(pkv, w)
-    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
     dec, pre, perm = oracle.mixed_permutation(w.qo_indptr, max_prefill_rows=4)
     assert np.array_equal(plan.permutation(), perm)
-    rows = _sample_rows(len(dec), 8, 5)
-    rows = [int(dec[i]) for i in rows] + [int(dec[np.argmax(w.kv_len[dec])])]
-    rng = np.random.default_rng(6)
-    toks = {r: np.array([0]) for r in rows}
-    for r in pre[:2]:
-        r = int(r)
-        rows.append(r)
-        toks[r] = np.unique(np.concatenate([[0, 1023], rng.integers(0, 1024, size=24)]))
-    ref = oracle_rows(w, rows, tokens=toks)
-    for r in rows:
-        sel = int(w.qo_indptr[r]) + toks[r]
-        compare(out[sel], lse[sel], ref[r][0], ref[r][1], f"mixed row {r} L={w.q_len[r]} N={w.kv_len[r]}")
+    ref_o, ref_l = oracle_all(w)
+    compare(out, lse, ref_o, ref_l, f"mixed_window full (all {w.total_q} tokens)", flat=True)
+    dq = np.asarray(w.qo_indptr)[dec]
+    compare(out[torch.from_numpy(dq.astype(np.int64)).to(gpu)], lse[torch.from_numpy(dq.astype(np.int64)).to(gpu)],
+            ref_o[dq], ref_l[dq], "mixed_window decode rows", flat=True)
+    compare(out[torch.from_numpy(perm.astype(np.int64)).to(gpu)], lse[torch.from_numpy(perm.astype(np.int64)).to(gpu)],
+            ref_o[perm], ref_l[perm], "mixed_window prompt tokens", flat=True)
