@@ -257,6 +257,25 @@ pkv_status pkv_plan_upload_stats(const pkv_plan* plan, int64_t stats[3]);
 pkv_status pkv_run(const pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* pkv_plan_upload + pkv_run without a caller workspace and without allocating
+ * anything, for callers that cannot allocate device memory: code under stream
+ * capture, tight serving loops, harnesses that forbid allocation.  The workspace
+ * is a static device array of pkv_noalloc_capacity() bytes (32 MiB), one per GPU,
+ * held until the process ends.  q, kv_cache_layer, out and lse are as for
+ * pkv_run; the plan's metadata reaches the array through the plan's staging
+ * ring, exactly as pkv_plan_upload does.
+ * Errors: PKV_E_CAPACITY if the plan's workspace_bytes exceed the array, or if
+ *   the plan's staging buffers are smaller than its metadata (pkv_plan_upload
+ *   sizes both whenever one grows: upload the plan, or a larger one, once
+ *   beforehand; a graph-static plan's metadata never grows); otherwise as
+ *   pkv_plan_upload and pkv_run.  Dense plans are PKV_E_INVALID.
+ * Every call on one GPU shares its array, which keeps the last call's contents:
+ * calls that overlap on one GPU (different streams, or threads without ordering)
+ * race.  Calls on one stream are ordered. */
+pkv_status pkv_run_noalloc(pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
+                           float* lse, void* stream);
+size_t pkv_noalloc_capacity(void);
+
 /* pkv_append_kv followed by pkv_run on the same stream (attn.dense requires_kv_write:
  * the step's K/V are stored before attention reads them).  k_new, v_new: bf16
  * [total_q, Hk, D], 16-byte aligned, not NULL.  Errors as pkv_run and

@@ -25,7 +25,8 @@ LIB = os.path.join(PKG, "libpkv.so")
 CEIL_LIB = os.path.join(PKG, "libpkv_ceilings.so")
 ARCH = "gfx950"
 
-SOURCES = ["plan.cpp", "capi.cpp", "decode.hip", "merge_append.hip", "prefill.hip", "mixed.hip"]
+SOURCES = ["plan.cpp", "capi.cpp", "decode.hip", "merge_append.hip", "prefill.hip", "mixed.hip",
+           "noalloc.hip"]
 CEIL_SOURCES = ["ceilings.hip"]
 
 

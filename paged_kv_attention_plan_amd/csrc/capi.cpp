@@ -12,6 +12,7 @@
 
 #include "kernels.h"
 #include "pkv.h"
+#include "handle.h"
 #include "plan.h"
 #include "stage.h"
 
@@ -19,10 +20,7 @@ namespace {
 
 thread_local std::string g_err;
 
-pkv_status fail(pkv_status s, std::string msg) {
-  g_err = std::move(msg);
-  return s;
-}
+using pkv::detail::fail;
 
 #define PKV_HIP(expr)                                                                    \
   do {                                                                                   \
@@ -39,21 +37,6 @@ constexpr std::chrono::seconds kStageTimeout(60);
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
-
-// Event pairs recorded around launches while timing is enabled.
-struct Timing {
-  bool enabled = false;
-  std::vector<hipEvent_t> pool;  // created lazily, reused after a read
-  size_t used = 0;
-  std::vector<int> kind;         // kernel kind of pair i (events 2i, 2i+1)
-};
-
-struct pkv_plan {
-  pkv::PlanData d;
-  pkv::StageRing ring;  // page-locked, host-coherent staging buffers of the uploads
-  void* uploaded_ws = nullptr;
-  mutable Timing timing;
-};
 
 namespace {
 
@@ -81,6 +64,11 @@ hipError_t timing_mark(const pkv_plan* p, hipStream_t s, int kind, bool begin) {
 }
 
 }  // namespace
+
+pkv_status pkv::detail::fail(pkv_status s, std::string msg) {
+  g_err = std::move(msg);
+  return s;
+}
 
 extern "C" {
 
@@ -264,9 +252,35 @@ static pkv_status check_workspace(const pkv_plan* plan, const void* ws, size_t w
   return PKV_OK;
 }
 
-pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream) {
-  g_err.clear();
-  if (plan == nullptr) return fail(PKV_E_INVALID, "plan must not be NULL");
+}  // extern "C"
+
+namespace {
+
+// (Re-)allocate a staging buffer of `cap` bytes plus its completion flags.
+// Page-locked and coherent: the upload kernel reads it over the host link,
+// never from a stale cache line of an earlier step, and its flag stores reach
+// the host.  The buffer must have no reader in flight.
+hipError_t grow_stage(pkv::Stage& s, size_t cap) {
+  if (s.host != nullptr) {
+    hipError_t e = hipHostFree(s.host);
+    if (e != hipSuccess) return e;
+  }
+  s.host = nullptr;
+  s.dev = nullptr;
+  s.cap = 0;
+  hipError_t e = hipHostMalloc(&s.host, cap + kUploadBlocks * sizeof(uint32_t), hipHostMallocCoherent);
+  if (e != hipSuccess) return e;
+  s.cap = cap;
+  e = hipHostGetDevicePointer(&s.dev, s.host, 0);
+  if (e != hipSuccess) return e;
+  for (int i = 0; i < kUploadBlocks; ++i) s.flags()[i] = s.seq;
+  return hipSuccess;
+}
+
+}  // namespace
+
+pkv_status pkv::detail::upload_meta(pkv_plan* plan, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream, bool may_allocate) {
   pkv_status st = check_workspace(plan, workspace, workspace_bytes);
   if (st != PKV_OK) return st;
   const size_t meta = plan->d.ws.meta_bytes;
@@ -276,22 +290,25 @@ pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_byt
   if (sp == nullptr)
     return fail(PKV_E_DEVICE, "a staging buffer's upload did not finish within 60 s");
   pkv::Stage& s = *sp;
+  if (s.cap < meta && !may_allocate)
+    return fail(PKV_E_CAPACITY,
+                "the plan's staging buffer holds " + std::to_string(s.cap) + " bytes and its metadata needs " +
+                    std::to_string(meta) + ": upload the plan (or a larger one) once with pkv_plan_upload, "
+                    "which sizes both staging buffers");
   if (s.cap < meta) {
-    if (s.host != nullptr) PKV_HIP(hipHostFree(s.host));
-    s.host = nullptr;
-    s.dev = nullptr;
-    s.cap = 0;
+    // Both buffers of the ring grow together (the other one after its last
+    // reader is done), so that an upload that may not allocate finds either
+    // one large enough.
+    pkv::Stage& other = plan->ring.stage[plan->ring.next ^ 1];
+    if (!pkv::wait_stage(other, kStageTimeout))
+      return fail(PKV_E_DEVICE, "a staging buffer's upload did not finish within 60 s");
     size_t cap = 4096;
     while (cap < meta) cap <<= 1;
-    // Coherent: the upload kernel reads it over the host link, never from a
-    // stale cache line of an earlier step, and its flag stores reach the host.
-    PKV_HIP(hipHostMalloc(&s.host, cap + kUploadBlocks * sizeof(uint32_t), hipHostMallocCoherent));
-    s.cap = cap;
-    PKV_HIP(hipHostGetDevicePointer(&s.dev, s.host, 0));
-    for (int i = 0; i < kUploadBlocks; ++i) s.flags()[i] = s.seq;
+    PKV_HIP(grow_stage(s, cap));
+    if (other.cap < cap) PKV_HIP(grow_stage(other, cap));
   }
   pkv::serialize_meta(plan->d, s.host);
-  hipStream_t st_ = static_cast<hipStream_t>(stream);
+  hipStream_t st_ = stream;
   pkv::UploadArgs ua{};
   ua.src = static_cast<const uint4*>(s.dev);
   ua.dst = static_cast<uint4*>(workspace);
@@ -304,6 +321,15 @@ pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_byt
   plan->ring.launched(blocks);
   plan->uploaded_ws = workspace;
   return PKV_OK;
+}
+
+extern "C" {
+
+pkv_status pkv_plan_upload(pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (plan == nullptr) return fail(PKV_E_INVALID, "plan must not be NULL");
+  return pkv::detail::upload_meta(plan, workspace, workspace_bytes, static_cast<hipStream_t>(stream),
+                                  true);
 }
 
 namespace {
@@ -425,12 +451,23 @@ pkv_status run_impl(const pkv_plan* plan, const void* q, const void* kv_cache_la
 
 }  // namespace
 
-pkv_status pkv_run(const pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
-                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
-  g_err.clear();
+}  // extern "C"
+
+pkv_status pkv::detail::run_plan(const pkv_plan* plan, const void* q, const void* kv_cache_layer,
+                                 void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
   pkv_status st = check_run(plan, q, kv_cache_layer, out, lse, workspace, workspace_bytes);
   if (st != PKV_OK || (plan->d.total_q == 0 && !plan->d.is_static)) return st;
   return run_impl(plan, q, kv_cache_layer, out, lse, workspace, stream);
+}
+
+extern "C" {
+
+pkv_status pkv_run(const pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
+                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  return pkv::detail::run_plan(plan, q, kv_cache_layer, out, lse, workspace, workspace_bytes,
+                               static_cast<hipStream_t>(stream));
 }
 
 pkv_status pkv_run_append(const pkv_plan* plan, const void* q, const void* k_new, const void* v_new,

@@ -84,6 +84,8 @@ def _load():
         "pkv_run_append": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
         "pkv_plan_metadata": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t]),
+        "pkv_run_noalloc": (C.c_int, [C.c_void_p] * 6),
+        "pkv_noalloc_capacity": (C.c_size_t, []),
         "pkv_context_only_views": (C.c_int, [C.c_int32, C.c_int32] + [P(C.c_int32)] * 9),
         "pkv_dense_plan_create": (C.c_int, [C.c_void_p, C.c_int32] + [P(C.c_int32)] * 4
                                   + [P(C.c_void_p), P(C.c_size_t)]),
@@ -110,7 +112,8 @@ EXPORTED = ("pkv_plan_params_init", "pkv_plan_create", "pkv_plan_update", "pkv_p
             "pkv_plan_decode_tiles", "pkv_plan_prefill_tiles", "pkv_plan_merges",
             "pkv_plan_write_slots", "pkv_plan_permutation", "pkv_plan_info", "pkv_plan_metadata",
             "pkv_plan_upload", "pkv_plan_upload_stats",
-            "pkv_run", "pkv_append_kv", "pkv_run_append", "pkv_context_only_views",
+            "pkv_run", "pkv_append_kv", "pkv_run_append", "pkv_run_noalloc", "pkv_noalloc_capacity",
+            "pkv_context_only_views",
             "pkv_dense_plan_create", "pkv_dense_plan_update", "pkv_dense_gather", "pkv_dense_run",
             "pkv_timing_enable", "pkv_timing_read",
             "pkv_last_error", "pkv_version")
@@ -303,6 +306,23 @@ def run(plan: Plan, q, kv_cache_layer, out, workspace, lse=None, stream=None):
                         _dev(out, "out", torch.bfloat16), _dev(lse, "lse", torch.float32),
                         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                         _stream(stream)))
+
+
+def run_noalloc(plan: Plan, q, kv_cache_layer, out, lse=None, stream=None):
+    """pkv_run_noalloc: upload + run with the library's static per-GPU workspace
+    (no allocation; the plan must have been uploaded once with plan_upload so
+    that its staging buffers hold its metadata)."""
+    import torch
+    _check_sizes(plan, kv_cache_layer, q=q, out=out, lse=lse)
+    _check(_lib.pkv_run_noalloc(plan.handle, _dev(q, "q", torch.bfloat16),
+                                _dev(kv_cache_layer, "kv_cache_layer", torch.bfloat16),
+                                _dev(out, "out", torch.bfloat16), _dev(lse, "lse", torch.float32),
+                                _stream(stream)))
+
+
+def noalloc_capacity() -> int:
+    """pkv_noalloc_capacity: bytes of the static workspace of run_noalloc."""
+    return int(_lib.pkv_noalloc_capacity())
 
 
 def run_append(plan: Plan, q, k_new, v_new, kv_cache_layer, out, workspace, lse=None, stream=None):
