@@ -52,7 +52,12 @@ WRITE_SCALE = 1.0
 CSRC = os.path.join(ROOT, "paged_kv_attention_plan_amd", "csrc")
 # the files whose text makes each kernel (its launch file and its device code)
 KERNEL_SOURCE = {"decode_kernel": ["decode.hip", "decode_body.cuh", "common.cuh"],
-                 "prefill_kernel": ["prefill.hip", "prefill_body.cuh", "common.cuh"]}
+                 "prefill_kernel": ["prefill.hip", "prefill_body.cuh", "common.cuh"],
+                 "merge_kernel": ["merge_append.hip", "common.cuh"],
+                 "append_kernel": ["merge_append.hip", "common.cuh"]}
+# oracle seconds each workload's CPU baseline may spend (about 30 s in all)
+CPU_BUDGET_S = {"tiny_decode": 2.0, "gqa_decode": 6.0, "long_decode": 6.0, "ragged_prefill": 8.0,
+                "mixed_window": 8.0}
 
 DESCR = {
     "tiny_decode": "tiny decode: 4 requests, Hq 4 / Hk 2, D 64, page 16, kv_len U[1,100]",
@@ -147,6 +152,33 @@ def work_of(w):
     qo_bytes = int(is_dec.sum()) * Hq * D * 2 * 2
     flops = int(vis[~is_dec].sum()) * Hq * 4 * D
     return {"kv_bytes": kv_bytes, "decode_bytes": kv_bytes + qo_bytes, "prefill_flops": flops}
+
+
+def aux_bytes(plan, w, appended):
+    """Algorithmic bytes per launch of the merge (every partial output and LSE
+    read once, the merged bf16 output and fp32 LSE written once) and of the
+    append (each new K and V row read once and written once)."""
+    g, D = w.num_qo_heads // w.num_kv_heads, w.head_dim
+    m = plan.merges()
+    chunks = int(m["n_chunks"].sum()) if len(m) else 0
+    merge = g * (chunks * (D * 4 + 4) + len(m) * (D * 2 + 4))
+    append = 2 * 2 * w.total_q * w.num_kv_heads * D * 2 if appended else 0
+    return {"merge_kernel": merge, "append_kernel": append}
+
+
+def aux_block(kt_ms, nbytes, workload):
+    """µs distribution, achieved GB/s and counter traffic of one small kernel."""
+    res = {}
+    for kind, kname in (("merge", "merge_kernel"), ("append", "append_kernel")):
+        ts = kt_ms.get(kind) or []
+        if not ts or not nbytes[kname]:
+            continue
+        us = mean_ms(ts) * 1e3
+        res[kname] = {"us": stats(ts, 1e3), "bytes_per_launch": nbytes[kname],
+                      "achieved_GBps": round(nbytes[kname] / (us * 1e-6) / 1e9, 1),
+                      "frac_hbm_peak": round(nbytes[kname] / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "traffic": traffic_of(kname, workload)}
+    return res
 
 
 class Runner:
@@ -469,42 +501,74 @@ def probe_ceilings(dev):
             "read": "streaming read of 2 GiB, 512 x 256 threads, 4 x 16-byte loads in flight, best of 5"}
 
 
-def cpu_baseline(runner, unit, budget_s=12.0):
-    """The oracle, timed on the host on the first rows of the same inputs until
-    about budget_s seconds of work; reported in the metric's unit (GB/s of KV
-    read for decode workloads, TFLOP/s for prefill)."""
-    import torch
-    import oracle
-    w = runner.w
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
         blas = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
-        cores = max(blas) if blas else 1
+        return max(blas) if blas else 1
     except Exception:
-        cores = 1
+        return 1
+
+
+def cpu_baseline(runner, budget_s):
+    """The oracle, timed on the host over the rows of the same inputs, in
+    order, until about budget_s seconds of work (decode rows and prompt rows
+    each get half when a workload has both).  Decode rows are reported in GB/s
+    of KV read, prompt rows in TFLOP/s; oracle seconds for the whole workload
+    are extrapolated from the sample by its share of the work."""
+    import torch
+    import oracle
+    w = runner.w
     vis = visible_counts(w)
-    done, kv_bytes, flops, elapsed = 0, 0, 0, 0.0
+    groups = {"decode": [], "prefill": []}
     for r in range(w.batch):
-        pages = w.kv_indices[w.kv_indptr[r]:w.kv_indptr[r + 1]]
-        sub = w.cache[torch.from_numpy(pages.astype(np.int64)).to(w.cache.device)].cpu()
-        q0, q1 = int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])
-        sub_q = w.q[q0:q1].cpu()
-        t0 = time.perf_counter()
-        oracle.attention_rows(sub_q, sub, w.page_size, np.array([0, len(pages)]),
-                              np.arange(len(pages)), w.last_page_len[r:r + 1],
-                              num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
-                              qo_indptr=np.array([0, q1 - q0]), causal=w.causal,
-                              window_left=w.window_left)
-        elapsed += time.perf_counter() - t0
-        kv_bytes += int(vis[q0:q1].max(initial=0)) * w.num_kv_heads * w.head_dim * 4
-        flops += int(vis[q0:q1].sum()) * w.num_qo_heads * 4 * w.head_dim
-        done += 1
-        if elapsed >= budget_s:
-            break
-    value = kv_bytes / elapsed / 1e9 if unit == "GB/s" else flops / elapsed / 1e12
-    return {"value": round(value, 6), "unit": unit, "cores": int(cores), "kind": "oracle",
-            "sample": f"first {done} of {w.batch} requests of the same seeded input, every query "
-                      f"head (float64 numpy), {elapsed:.1f} s"}
+        L = int(w.q_len[r])
+        if L == 1 and w.kind in ("decode", "mixed"):
+            groups["decode"].append(r)
+        elif L > 0:
+            groups["prefill"].append(r)
+    groups = {k: v for k, v in groups.items() if v}
+    res = {}
+    for kind, rows in groups.items():
+        share = budget_s / len(groups)
+        work = lambda r: (int(vis[int(w.qo_indptr[r])]) * w.num_kv_heads * w.head_dim * 4
+                          if kind == "decode" else
+                          int(vis[int(w.qo_indptr[r]):int(w.qo_indptr[r + 1])].sum())
+                          * w.num_qo_heads * 4 * w.head_dim)
+        total = sum(work(r) for r in rows)
+        done, amount, elapsed = 0, 0, 0.0
+        for r in rows:
+            pages = w.kv_indices[w.kv_indptr[r]:w.kv_indptr[r + 1]]
+            sub = w.cache[torch.from_numpy(pages.astype(np.int64)).to(w.cache.device)].cpu()
+            q0, q1 = int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])
+            sub_q = w.q[q0:q1].cpu()
+            t0 = time.perf_counter()
+            oracle.attention_rows(sub_q, sub, w.page_size, np.array([0, len(pages)]),
+                                  np.arange(len(pages)), w.last_page_len[r:r + 1],
+                                  num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+                                  qo_indptr=np.array([0, q1 - q0]), causal=w.causal,
+                                  window_left=w.window_left)
+            elapsed += time.perf_counter() - t0
+            amount += work(r)
+            done += 1
+            if elapsed >= share:
+                break
+        unit = "GB/s" if kind == "decode" else "TFLOP/s"
+        value = amount / elapsed / (1e9 if kind == "decode" else 1e12)
+        res[kind] = {"value": round(value, 6), "unit": unit, "oracle_s": round(elapsed, 2),
+                     "rows": f"{done} of {len(rows)}",
+                     "oracle_s_whole_workload_est": round(elapsed * total / max(amount, 1), 1)}
+    return {"cores": int(blas_threads()), "kind": "oracle", "float": "float64 numpy",
+            **res}
+
+
+def headline_cpu_baseline(cb, unit, name):
+    """The contract's cpu_baseline object from a cpu_baseline() result."""
+    part = cb["decode" if unit == "GB/s" else "prefill"]
+    return {"value": part["value"], "unit": part["unit"], "cores": cb["cores"], "kind": "oracle",
+            "sample": f"{name}: first {part['rows']} requests of the same seeded input, every "
+                      f"query head (float64 numpy), {part['oracle_s']} s; about "
+                      f"{part['oracle_s_whole_workload_est']} s for the whole workload"}
 
 
 @contextlib.contextmanager
@@ -522,7 +586,19 @@ def no_gc_pause():
             gc.enable()
 
 
-def secondary(name, dev, steps, warmup):
+def prefill_roofline(kt_ms, flops, workload):
+    """The roofline object of the prefill kernel from its event-timed launches."""
+    ts = kt_ms["prefill"]
+    pms = mean_ms(ts)
+    achieved = flops / (pms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
+            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
+            "traffic": traffic_of("prefill_kernel", workload), "kernel": "prefill_kernel",
+            "kernel_us": round(pms * 1e3, 2), "kernel_us_dist": stats(ts, 1e3),
+            "flops_per_launch": flops, "workload": workload}
+
+
+def secondary(name, dev, steps, warmup, with_cpu=False):
     r = Runner(name, dev)
     ms, _ = r.time_steps(steps, warmup)
     if r.graph:  # no per-kernel events inside a replay: compare whole steps with eager ones
@@ -549,10 +625,17 @@ def secondary(name, dev, steps, warmup):
         res["prefill_kernel_us"] = round(pms * 1e3, 2)
         res["prefill_TFLOPs_per_kernel"] = round(r.work["prefill_flops"] / (pms * 1e-3) / 1e12, 1)
         res["prefill_frac_mfma_peak"] = round(res["prefill_TFLOPs_per_kernel"] / MFMA_BF16_PEAK_TFS, 4)
+        res["roofline"] = prefill_roofline(kt, r.work["prefill_flops"], name)
     elif r.work["prefill_flops"]:  # a mixed plan's one launch, timed as "decode"
         fms = mean_ms(kt["decode"])
         res["fused_decode_prefill_launch"] = True
         res["prefill_TFLOPs_in_fused_launch"] = round(r.work["prefill_flops"] / (fms * 1e-3) / 1e12, 1)
+    if not r.dense:
+        aux = aux_block(kt, aux_bytes(r.plan, r.w, r.append), name)
+        if aux:
+            res["aux_kernels"] = aux
+    if with_cpu and name in CPU_BUDGET_S:
+        res["cpu_baseline"] = cpu_baseline(r, CPU_BUDGET_S[name])
     del r
     import torch
     torch.cuda.empty_cache()
@@ -607,13 +690,7 @@ def main():
                 "bytes_per_launch": w["decode_bytes"]}
     else:  # prefill only: FLOP per second, prefill kernel on bf16 MFMA
         value, unit = w["prefill_flops"] / (ms * 1e-3) / 1e12, "TFLOP/s"
-        pre_ms = mean_ms(kt["prefill"])
-        achieved = w["prefill_flops"] / (pre_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
-                "traffic": traffic_of("prefill_kernel", args.config), "kernel": "prefill_kernel",
-                "kernel_us": round(pre_ms * 1e3, 2),
-                "flops_per_launch": w["prefill_flops"]}
+        roof = prefill_roofline(kt, w["prefill_flops"], args.config)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -637,17 +714,33 @@ def main():
         "host": r.host_times(args.steps),
         "plan": r.plan.info(),
     }
+    if not r.dense and not r.graph:
+        aux = aux_block(kt, aux_bytes(r.plan, r.w, r.append), args.config)
+        if aux:
+            line["aux_kernels"] = aux
+    per_cfg = {}
+    if not args.no_cpu_baseline and args.config in CPU_BUDGET_S:
+        per_cfg[args.config] = cpu_baseline(r, CPU_BUDGET_S[args.config])
+        line["cpu_baseline"] = headline_cpu_baseline(per_cfg[args.config], unit, args.config)
+    del r
+    torch.cuda.empty_cache()
     if not args.no_secondary:
         sec = []
-        for name in ("long_decode", "ragged_prefill", "mixed_window", "gqa_decode_context_only",
-                     "ragged_prefill_dense", "tiny_decode_graph"):
+        for name in ("tiny_decode", "long_decode", "ragged_prefill", "mixed_window",
+                     "gqa_decode_context_only", "ragged_prefill_dense", "tiny_decode_graph"):
             if name != args.config:
-                sec.append(secondary(name, dev, max(5, args.steps // 5), 5))
+                res = secondary(name, dev, max(20, args.steps // 2), 5,
+                                with_cpu=not args.no_cpu_baseline)
+                if "cpu_baseline" in res:
+                    per_cfg[name] = res.pop("cpu_baseline")
+                if name == "ragged_prefill" and "roofline" in res:
+                    line["roofline_prefill"] = res["roofline"]
+                sec.append(res)
         line["secondary"] = sec
+    if per_cfg:
+        line["cpu_baseline_per_config"] = per_cfg
     if not args.no_ceilings:
         line["measured_ceilings"] = ceilings(dev)
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(r, unit)
     print(json.dumps(line), flush=True)
 
 

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import synth
-from gpu_common import compare, gpu_run, oracle_rows, say
+from gpu_common import compare, gpu_run, oracle_all, say
 
 pytestmark = pytest.mark.gpu
 
@@ -125,7 +125,7 @@ def test_dense_run_matches_oracle_and_paged(pkv, gpu, case):
 
 
 def test_full_ragged_prefill_dense(pkv, gpu):
-    say("case ragged_prefill dense (full size): bit-identical to paged, oracle on sampled rows")
+    say("case ragged_prefill dense (full size): bit-identical to paged, every element against the oracle")
     w = synth.make_workload("ragged_prefill", device=gpu)
     plan, ws, k, v, kf, vf, cu_q, cu_k = _dense(pkv, w)
     out = torch.empty_like(w.q)
@@ -134,11 +134,5 @@ def test_full_ragged_prefill_dense(pkv, gpu):
     p_out, p_lse, _, _ = gpu_run(pkv, w)
     assert torch.equal(out.view(torch.int16), p_out.view(torch.int16))
     assert torch.equal(lse.view(torch.int32), p_lse.view(torch.int32))
-    rng = np.random.default_rng(5)
-    rows = sorted(rng.choice(w.batch, size=3, replace=False).tolist())
-    toks = {r: sorted(rng.choice(int(w.q_len[r]), size=min(24, int(w.q_len[r])),
-                                 replace=False).tolist()) for r in rows}
-    ref = oracle_rows(w, rows, tokens=toks)
-    for r in rows:
-        sel = torch.tensor([int(w.qo_indptr[r]) + t for t in toks[r]], device=gpu)
-        compare(out[sel], lse[sel], ref[r][0], ref[r][1], f"ragged dense row {r}", flat=True)
+    ref_o, ref_l = oracle_all(w)
+    compare(out, lse, ref_o, ref_l, f"ragged_prefill dense full (all {w.total_q} tokens)", flat=True)
