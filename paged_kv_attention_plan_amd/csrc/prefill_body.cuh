@@ -54,6 +54,8 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+__device__ __forceinline__ float max3f(float x, float y, float z) { return fmaxf(fmaxf(x, y), z); }
+
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   const f32x2_t v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
@@ -220,10 +222,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
   for (int b = 0; b < NQB; ++b)
 #pragma unroll
     for (int d = 0; d < DBLK; ++d) oacc[b][d] = f32x4_t{};
-  float m_run[NQB], l_run[NQB];  // m_run in exp2 units (scaled)
+  // Running max per query in exp2 units, kept negated (nm = -m, the exponent's
+  // offset), and the raw-score threshold above which it must move:
+  // th = (m + slack) / c.
+  const float inv_c = 1.f / a.scale_log2;
+  float nm[NQB], th[NQB], l_run[NQB];
 #pragma unroll
   for (int b = 0; b < NQB; ++b) {
-    m_run[b] = -1e30f;
+    nm[b] = 1e30f;
+    th[b] = -1e30f;
     l_run[b] = 0.f;
   }
 
@@ -326,12 +333,16 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
       }
     }
   };
-  // Does the step at kbase cross the causal diagonal, the window edge or the
-  // row end?  (uniform)
-  auto needs_mask = [&](int kbase) {
-    return (kbase + BN - 1 > (causal ? p_first : kv_len - 1)) || (kbase + BN > kv_len) ||
-           (wl >= 0 && kbase < p_last - wl);
-  };
+  // Does step t cross the causal diagonal, the row end (both from step t_a
+  // on) or the window edge (steps before t_b)?  A step at key kbase needs
+  // masks when kbase + BN - 1 passes the first query's last visible key or
+  // kbase + BN passes the row end, or kbase is below the last query's window.
+  // (uniform; kstart <= the first visible key, so mask_x >= -BN)
+  const int mask_x = min((causal ? p_first : kv_len - 1) - kstart - (BN - 1), kv_len - kstart - BN);
+  const int t_a = (mask_x + BN) / BN;
+  const int mask_y = wl >= 0 ? p_last - wl - kstart : 0;
+  const int t_b = mask_y > 0 ? (mask_y + BN - 1) / BN : 0;
+  auto needs_mask = [&](int t) { return t >= t_a || t < t_b; };
   // Scores of keys outside [lo_j, hi_j] become -inf.
   auto apply_mask = [&](f32x4_t (&sacc)[NQB][2], int kbase) {
     const int k0 = kbase + 4 * lg;
@@ -354,27 +365,29 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
   auto lanemax = [&](const f32x4_t (&sacc)[NQB][2], float (&lm)[NQB]) {
 #pragma unroll
     for (int b = 0; b < NQB; ++b) {
-      const float x = fmaxf(fmaxf(sacc[b][0][0], sacc[b][0][1]), fmaxf(sacc[b][0][2], sacc[b][0][3]));
-      const float y = fmaxf(fmaxf(sacc[b][1][0], sacc[b][1][1]), fmaxf(sacc[b][1][2], sacc[b][1][3]));
-      lm[b] = fmaxf(x, y);
+      lm[b] = max3f(max3f(sacc[b][0][0], sacc[b][0][1], sacc[b][0][2]),
+                    max3f(sacc[b][0][3], sacc[b][1][0], sacc[b][1][1]),
+                    fmaxf(sacc[b][1][2], sacc[b][1][3]));
     }
   };
-  // Move the running maxima (and rescale O, l) only when some score exceeds
-  // its query's running max by more than the slack.  Each lane tests its own
+  // Move the running maxima (and rescale O, l) only when some raw score
+  // exceeds its query's threshold, i.e. the running max by more than the
+  // slack after scaling.  Each lane tests its own
   // scores, so the column maxima across the four row groups (two exchanges
   // per block) are formed only on that rare branch (uniform over the wave);
   // there every query's max moves to its column max, which is always exact.
   auto update_max = [&](const float (&lm)[NQB]) {
     bool need = false;
 #pragma unroll
-    for (int b = 0; b < NQB; ++b) need |= lm[b] * c > m_run[b] + kRescaleSlack;
+    for (int b = 0; b < NQB; ++b) need |= lm[b] > th[b];
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
       for (int b = 0; b < NQB; ++b) {
         const float mr = max_x32(max_x16(lm[b]));
-        const float mn = fmaxf(m_run[b], mr * c);
-        const float alpha = fast_exp2(m_run[b] - mn);
-        m_run[b] = mn;
+        const float mn = fmaxf(-nm[b], mr * c);
+        const float alpha = fast_exp2(-nm[b] - mn);
+        nm[b] = -mn;
+        th[b] = (mn + kRescaleSlack) * inv_c;
         l_run[b] *= alpha;
 #pragma unroll
         for (int d = 0; d < DBLK; ++d) oacc[b][d] *= alpha;
@@ -401,7 +414,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
   f32x4_t sa[NQB][2], sb[NQB][2];
   {
     qk(0, sa);
-    if (needs_mask(kstart)) apply_mask(sa, kstart);
+    if (needs_mask(0)) apply_mask(sa, kstart);
     float lm[NQB];
     lanemax(sa, lm);
     update_max(lm);
@@ -441,7 +454,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
       // e / (4 NQB), element e % 4
       auto expo = [&](int e) {
         const int b = (e / 4) % NQB, kb = e / (4 * NQB), r = e % 4;
-        const float p = fast_exp2(fmaf(cur[b][kb][r], c, -m_run[b]));
+        const float p = fast_exp2(fmaf(cur[b][kb][r], c, nm[b]));
         pe[b][kb][r] = p;
         l_run[b] += p;  // fp32 P: a sum of the bf16-rounded P misses the LSE bound
         if (r & 1) pb[b][2 * kb + r / 2] = cvt_pk_bf16(pe[b][kb][r - 1], p);
@@ -462,8 +475,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
 #pragma unroll
       for (int e = 0; e < NEA; ++e) expo(e);
     }
-    const int knext = kstart + (i + 1) * BN;
-    if (needs_mask(knext)) apply_mask(nxt, knext);
+    if (needs_mask(i + 1)) apply_mask(nxt, kstart + (i + 1) * BN);
     // ---- O += P V on the matrix cores while the VALU finds S(i+1)'s maxima ----
     float lm[NQB];
     {
@@ -485,11 +497,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
           const int k = db * NQB + b;
           oacc[b][db] = mfma16(vf[db % (KA + 1)], pb[b], oacc[b][db]);
           // the lane's maxima of S(i+1) in the first NQB slots
-          if (k < NQB) {
-            const float x = fmaxf(fmaxf(nxt[k][0][0], nxt[k][0][1]), fmaxf(nxt[k][0][2], nxt[k][0][3]));
-            const float y = fmaxf(fmaxf(nxt[k][1][0], nxt[k][1][1]), fmaxf(nxt[k][1][2], nxt[k][1][3]));
-            lm[k] = fmaxf(x, y);
-          }
+          if (k < NQB)
+            lm[k] = max3f(max3f(nxt[k][0][0], nxt[k][0][1], nxt[k][0][2]),
+                          max3f(nxt[k][0][3], nxt[k][1][0], nxt[k][1][1]),
+                          fmaxf(nxt[k][1][2], nxt[k][1][3]));
         }
       }
     }
@@ -527,7 +538,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
         *reinterpret_cast<u32x2_t*>(op + 16 * db) = w2;
       }
       if (a.lse != nullptr && lg == 0)
-        a.lse[qi] = (m_run[b] + log2f(l_tot)) * kLn2;
+        a.lse[qi] = (log2f(l_tot) - nm[b]) * kLn2;
     }
   }
 }
