@@ -677,7 +677,10 @@ def main():
     ms, wall_ms = r.time_steps(args.steps, args.warmup)
     kt = r.kernel_times(args.steps)
     w = r.work
-    if w["kv_bytes"]:  # decode rows present: KV bytes per second, decode kernel on HBM
+    if r.graph:  # a replayed graph records no per-kernel events: whole steps only
+        value, unit = w["kv_bytes"] / (ms * 1e-3) / 1e9, "GB/s"
+        roof = None
+    elif w["kv_bytes"]:  # decode rows present: KV bytes per second, decode kernel on HBM
         value, unit = w["kv_bytes"] / (ms * 1e-3) / 1e9, "GB/s"
         dec_ms = mean_ms(kt["decode"])
         achieved = w["decode_bytes"] / (dec_ms * 1e-3) / 1e9
