@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256, 2) void mixed_kernel(DecodeArgs da, PrefillArg
     dec::decode_wave<D, G, ONE_PAGE_PER_ITER>(da, blockIdx.x * dec::kWaves + wave, lane);
     return;
   }
-  pre::prefill_tile<D, true, false>(pa, (int)blockIdx.x - dec_blocks);
+  pre::prefill_tile<D, true, false, false>(pa, (int)blockIdx.x - dec_blocks);
 }
 
 template <int D, int G>

@@ -129,7 +129,10 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
 // DENSE (with WAVE_PAGE): the keys are contiguous rows of k_dense / v_dense
 // starting at the tile's page_base; the row acts as one page.
 // Tile `tile` of the prefill tile list, by a workgroup of 256 threads.
-template <int D, bool WAVE_PAGE, bool DENSE>
+// PRIO: raise the wave's priority for the softmax and the copy issue (the
+// prefill launch, where both waves of a SIMD run prefill tiles); off in the
+// fused mixed-step launch, where it would hold back the decode waves.
+template <int D, bool WAVE_PAGE, bool DENSE, bool PRIO = true>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
   constexpr int NQB = kNqb;
   constexpr int BN = 32;              // keys per step
@@ -436,7 +439,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
   auto step = [&](f32x4_t (&cur)[NQB][2], f32x4_t (&nxt)[NQB][2], int i, int bi) {
     const int bn = bi + 1 == NBUF ? 0 : bi + 1;   // (i + 1) % NBUF
     const int bp = bi == 0 ? NBUF - 1 : bi - 1;   // (i + PF) % NBUF = (i - 1) % NBUF
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(2);
     issue(i + PF, bp);
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     u32x4_t pb[NQB];
     // ---- S(i+1) on the matrix cores while the VALU turns S(i) into P ----
     {
@@ -457,7 +462,12 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
         const float p = fast_exp2(fmaf(cur[b][kb][r], c, nm[b]));
         pe[b][kb][r] = p;
         l_run[b] += p;  // fp32 P: a sum of the bf16-rounded P misses the LSE bound
-        if (r & 1) pb[b][2 * kb + r / 2] = cvt_pk_bf16(pe[b][kb][r - 1], p);
+        if (r & 1) {
+          pb[b][2 * kb + r / 2] = cvt_pk_bf16(pe[b][kb][r - 1], p);
+          // keep the softmax here, inside the raised-priority window below,
+          // instead of letting the compiler sink it past the mask branch
+          asm volatile("" : "+v"(pb[b][2 * kb + r / 2]), "+v"(l_run[b]));
+        }
       };
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) {
@@ -471,9 +481,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
       }
       // P of step i.  On the VALU, after the matrix work above is issued: the
       // other wave on the SIMD (another workgroup, at another phase) keeps
-      // the matrix cores busy meanwhile.
+      // the matrix cores busy meanwhile.  With PRIO the wave's priority is
+      // raised for this vector work (and for the copy issue), so that when both
+      // waves of a SIMD are ready the softmax goes first and the other wave's
+      // MFMAs fill the matrix pipe behind it (about 1 % faster, alternated on
+      // one box).
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int e = 0; e < NEA; ++e) expo(e);
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     }
     if (needs_mask(i + 1)) apply_mask(nxt, kstart + (i + 1) * BN);
     // ---- O += P V on the matrix cores while the VALU finds S(i+1)'s maxima ----
