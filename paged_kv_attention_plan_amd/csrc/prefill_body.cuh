@@ -543,6 +543,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
     const float l_tot = sum_x32(sum_x16(l_run[b]));
     int qh, tl;
     pair_of(b, qh, tl);
+    // recomputed here rather than kept from the q loads across the key loop
+    // (which would hold 64-bit addresses in scratch)
+    asm volatile("" : "+v"(tl), "+v"(qh));
     const int64_t qi = (int64_t)(q_base + q_start + tl) * Hq + qh;
     if (tl < q_count) {
       const float inv = 1.f / l_tot;
