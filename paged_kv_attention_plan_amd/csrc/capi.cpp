@@ -70,6 +70,8 @@ pkv_status pkv::detail::fail(pkv_status s, std::string msg) {
   return s;
 }
 
+void pkv::detail::clear_error() { g_err.clear(); }
+
 extern "C" {
 
 const char* pkv_last_error(void) { return g_err.c_str(); }

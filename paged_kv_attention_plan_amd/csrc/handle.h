@@ -31,6 +31,8 @@ namespace detail {
 
 // Set the thread's error message; returns s.
 pkv_status fail(pkv_status s, std::string msg);
+// Clear it (at the start of every entry point).
+void clear_error();
 
 // Serialise the plan's metadata into its staging ring and enqueue the upload
 // kernel that copies it to the head of `workspace` (the body of

@@ -53,6 +53,7 @@ size_t pkv_noalloc_capacity(void) { return kScratchBytes; }
 
 pkv_status pkv_run_noalloc(pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
                            float* lse, void* stream) {
+  pkv::detail::clear_error();
   if (plan == nullptr) return pkv::detail::fail(PKV_E_INVALID, "plan must not be NULL");
   if (plan->d.dense)
     return pkv::detail::fail(PKV_E_INVALID, "a dense plan runs through pkv_dense_gather / pkv_dense_run");

@@ -375,10 +375,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
   };
   // Move the running maxima (and rescale O, l) only when some raw score
   // exceeds its query's threshold, i.e. the running max by more than the
-  // slack after scaling.  Each lane tests its own
-  // scores, so the column maxima across the four row groups (two exchanges
-  // per block) are formed only on that rare branch (uniform over the wave);
-  // there every query's max moves to its column max, which is always exact.
+  // slack after scaling.  Each lane tests its own scores, so the column
+  // maxima across the four row groups (two exchanges per block) are formed
+  // only on that rare branch (uniform over the wave); there every query's max
+  // moves to its column max, which is always exact.
   auto update_max = [&](const float (&lm)[NQB]) {
     bool need = false;
 #pragma unroll
