@@ -447,9 +447,11 @@ def ceilings(dev):
 
 def probe_ceilings(dev):
     """The two rates the attention kernels are bound by, from the probe
-    library built beside libpkv.so: a register-only bf16 MFMA loop
+    library built beside libpkv.so: register-only bf16 MFMA loops
     (v_mfma_f32_32x32x16_bf16, 4096 workgroups of 4 waves, 2048 rounds of four
-    independent products each) and a streaming read of 2 GiB (512 workgroups
+    independent products each; the same with v_mfma_f32_16x16x32_bf16; and that
+    one with operands that change between products, with the shader clock
+    measured over each) and a streaming read of 2 GiB (512 workgroups
     of 256 threads, four 16-byte non-temporal loads in flight per thread: the
     best of a sweep of launch shapes), each the best of 5 launches after
     warm-up launches that bring the clocks up."""
@@ -460,7 +462,9 @@ def probe_ceilings(dev):
         return {"probes": "libpkv_ceilings.so not built"}
     lib = ctypes.CDLL(path)
     lib.pkv_ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    lib.pkv_ceiling_mfma16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.pkv_ceiling_mfma16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p]
+    lib.pkv_ceiling_mfma16_rot.argtypes = lib.pkv_ceiling_mfma16.argtypes
     lib.pkv_ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                      ctypes.c_int, ctypes.c_void_p]
     stream = torch.cuda.current_stream(dev)
@@ -483,9 +487,26 @@ def probe_ceilings(dev):
     ms = best_ms(lambda: lib.pkv_ceiling_mfma(ctypes.c_void_p(sink.data_ptr()), blocks, iters, sh),
                  warm=3)
     mfma_tfs = blocks * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
-    ms = best_ms(lambda: lib.pkv_ceiling_mfma16(ctypes.c_void_p(sink.data_ptr()), blocks, iters, sh),
+    clk = torch.zeros(2, dtype=torch.int64, device=dev)
+    wall_hz = lib.pkv_ceiling_wallclock_khz() * 1e3
+
+    def clock_ghz():  # shader clock over the launches since the last call
+        c = clk.tolist()
+        clk.zero_()
+        return round(c[0] / c[1] * wall_hz / 1e9, 3) if c[1] > 0 and wall_hz > 0 else None
+
+    ms = best_ms(lambda: lib.pkv_ceiling_mfma16(ctypes.c_void_p(sink.data_ptr()),
+                                                ctypes.c_void_p(clk.data_ptr()), blocks, iters, sh),
                  warm=3)
     mfma16_tfs = blocks * 4 * iters * 8 * 16384 / (ms * 1e-3) / 1e12
+    mfma16_ghz = clock_ghz()
+    # changing operands, long enough (about 12 ms a launch) for the clock to settle
+    rot_blocks, rot_iters = 2048, 20000
+    ms = best_ms(lambda: lib.pkv_ceiling_mfma16_rot(ctypes.c_void_p(sink.data_ptr()),
+                                                    ctypes.c_void_p(clk.data_ptr()), rot_blocks,
+                                                    rot_iters, sh), warm=1)
+    rot_tfs = rot_blocks * 4 * rot_iters * 8 * 16384 / (ms * 1e-3) / 1e12
+    rot_ghz = clock_ghz()
     nbytes = 2 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(3)
     ms = best_ms(lambda: lib.pkv_ceiling_read(ctypes.c_void_p(src.data_ptr()), nbytes,
@@ -498,6 +519,13 @@ def probe_ceilings(dev):
             "mfma16_loop_TFLOPs": round(mfma16_tfs, 1),
             "mfma16_loop": "the same with v_mfma_f32_16x16x32_bf16 (the prefill kernel's shape), "
                            "8 chains per wave, best of 5",
+            "mfma16_loop_clock_GHz": mfma16_ghz,
+            "mfma16_rotating_TFLOPs": round(rot_tfs, 1),
+            "mfma16_rotating_clock_GHz": rot_ghz,
+            "mfma16_rotating": "the 16x16x32 loop with 16 pseudo-random operand pairs per lane taken "
+                               "in turn (operands change between products, as on real data), "
+                               "8192 waves x 160000 products, best of 5; the clock is s_memtime "
+                               "cycles over s_memrealtime ticks",
             "read": "streaming read of 2 GiB, 512 x 256 threads, 4 x 16-byte loads in flight, best of 5"}
 
 
