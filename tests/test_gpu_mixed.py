@@ -52,6 +52,24 @@ CASES = [
 ]
 
 
+def _random_mixed_shapes(n=8, seed=4343):
+    """Seeded mixed shapes: head dims, decode-supported groups, page sizes on
+    both sides of the one-launch threshold (16), windows."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        D = int(rng.choice([64, 128]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        hk = int(rng.choice([1, 2, 4]))
+        ps = int(rng.choice([1, 4, 8, 16, 32, 64]))
+        wl = int(rng.choice([-1, -1, 0, 25, 400]))
+        out.append((620 + k, D, g * hk, hk, ps, wl))
+    return out
+
+
+CASES += _random_mixed_shapes()
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}-D{c[1]}-g{c[2]//c[3]}-ps{c[4]}-w{c[5]}")
 def test_mixed_equals_decode_plus_prefill(pkv, gpu, case):
     seed, D, hq, hk, ps, wl = case

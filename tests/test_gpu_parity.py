@@ -82,6 +82,36 @@ def test_decode_small(pkv, gpu, case):
     compare(out, lse, ref_o, ref_l, f"decode s{seed}")
 
 
+def _random_decode_shapes(n=16, seed=4141):
+    """Seeded decode shapes across head dims, GQA groups, KV head counts that do
+    and do not fill a 4-wave workgroup, page sizes 1..256, windows, stale data
+    and forced splits."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for k in range(n):
+        D = int(rng.choice([64, 128]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        hk = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        ps = int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128, 256]))
+        wl = int(rng.choice([-1, -1, 0, 9, 200]))
+        out.append((150 + k, D, g * hk, hk, ps, wl, "nan" if k % 2 else "zero", bool(k % 3)))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_decode_shapes(),
+                         ids=lambda c: f"s{c[0]}-D{c[1]}-g{c[2]//c[3]}-ps{c[4]}-w{c[5]}-split{int(c[7])}")
+def test_decode_random_shapes(pkv, gpu, case):
+    seed, D, hq, hk, ps, wl, stale, split = case
+    say(f"case decode sweep seed={seed} D={D} Hq={hq} Hk={hk} ps={ps} window={wl} split={split}")
+    w = synth.random_case(seed, kind="decode", batch=7, num_qo_heads=hq, num_kv_heads=hk,
+                          head_dim=D, page_size=ps, max_kv=900, window_left=wl, stale=stale,
+                          device=gpu)
+    kw = dict(num_cus=32, decode_waves_per_cu=16, decode_min_chunk_pages=1) if split else {}
+    out, lse, plan, _ = gpu_run(pkv, w, **kw)
+    ref_o, ref_l = _full_oracle(w)
+    compare(out, lse, ref_o, ref_l, f"decode sweep s{seed}")
+
+
 PREFILL = [
     # (seed, head_dim, Hq, Hk, page_size, causal, window, stale)
     (200, 128, 32, 8, 16, True, -1, "nan"),
