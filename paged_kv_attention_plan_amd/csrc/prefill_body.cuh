@@ -247,6 +247,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
   const_as4_ptr<int32_t> cidx = as_const4(a.indices);
   const uint32_t row_bytes = (uint32_t)row_elems * 2u;
   const uint32_t head_bytes = (uint32_t)hk * D * 2u;
+  const uint32_t page_bytes = (uint32_t)(page_elems * 2);  // < 4 GiB: ps <= 256
+  const uint64_t v_bytes = (uint64_t)v_off * 2u;
+  const uint32_t lane_row_bytes = (uint32_t)(lane / SEGS) * row_bytes;  // lane's row in a copy
 
   // Copy map: copy j of wave w fills rows KW*w + RPI*j + lane/SEGS of the step,
   // physical segment lane % SEGS, with the source segment that the swizzle
@@ -262,19 +265,54 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
 
   // Issue the copies of step t (clamped to the last step, and each key to the
   // row's last key, so addresses stay inside the row; keys past the row are
-  // masked later) into buffer t % NBUF.  Every call issues exactly 2*NI copies
+  // masked later) into the buffer at byte offset boff (t % NBUF times BUFB) of
+  // the K and V rings.  Every call issues exactly 2*NI copies
   // per wave: the waits below count on it.
-  auto issue = [&](int t, int buf) {
-    t = t < ntiles ? t : ntiles - 1;
-    const int k0 = kstart + t * BN + KW * wave;        // multiple of KW
-    const int kb0 = k0 < kv_len ? k0 : kv_len - 1;    // first key actually read
-    const int room = kv_len - 1 - kb0;                // keys after kb0 in the row
+  auto issue = [&](int t, uint32_t boff) {
     const uint32_t mk = (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)(lds_k + buf * BUFB + KW * wave * ROWB));
+        (int)(lds_k + boff + KW * wave * ROWB));
     const uint32_t mv = (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)(lds_v + buf * BUFB + KW * wave * ROWB));
+        (int)(lds_v + boff + KW * wave * ROWB));
     if constexpr (DENSE || WAVE_PAGE) {
       // The wave's KW keys lie in one page (or one dense row): a uniform base.
+      const int kw0 = kstart + t * BN + KW * wave;
+      if (kw0 + KW <= kv_len) {
+        // All KW keys are in the row (every step but the row's last): no
+        // clamping, and the key's offset inside the page goes into the base.
+        // (A step past the tile's last reads keys of the row that no score
+        // uses.)
+        const char* kbase;
+        if constexpr (DENSE) {
+          kbase = reinterpret_cast<const char*>(a.k_dense) +
+                  (uint64_t)(uint32_t)(page_base + kw0) * row_bytes;
+        } else {
+          const uint32_t ib = ((uint32_t)page_base + ((uint32_t)kw0 >> ps_log2)) << 2;
+          const uint32_t pid = *reinterpret_cast<const_as4_ptr<uint32_t>>(
+              reinterpret_cast<const_as4_ptr<char>>(cidx) + ib);  // scalar load
+          kbase = reinterpret_cast<const char*>(a.cache) + (uint64_t)pid * page_bytes +
+                  (uint32_t)(kw0 & (ps - 1)) * row_bytes;
+        }
+        const char* vbase = DENSE ? reinterpret_cast<const char*>(a.v_dense) +
+                                        (uint64_t)(uint32_t)(page_base + kw0) * row_bytes
+                                  : kbase + v_bytes;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          int rwj;
+          const uint32_t src = copy_src(j, false, rwj);
+          dma16(lane_row_bytes + (uint32_t)(RPI * j) * row_bytes + src, kbase, mk + 1024u * j);
+        }
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          int rwj;
+          const uint32_t src = copy_src(j, true, rwj);
+          dma16(lane_row_bytes + (uint32_t)(RPI * j) * row_bytes + src, vbase, mv + 1024u * j);
+        }
+        return;
+      }
+      t = t < ntiles ? t : ntiles - 1;
+      const int k0 = kstart + t * BN + KW * wave;        // multiple of KW
+      const int kb0 = k0 < kv_len ? k0 : kv_len - 1;    // first key actually read
+      const int room = kv_len - 1 - kb0;                // keys after kb0 in the row
       const char* kbase;
       if constexpr (DENSE) {
         kbase = reinterpret_cast<const char*>(a.k_dense) + ((int64_t)page_base + kb0) * row_bytes;
@@ -300,6 +338,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
       }
     } else {
       // Pages shorter than the wave's keys: a page id per lane.
+      t = t < ntiles ? t : ntiles - 1;
+      const int k0 = kstart + t * BN + KW * wave;        // multiple of KW
+      const int kb0 = k0 < kv_len ? k0 : kv_len - 1;    // first key actually read
+      const int room = kv_len - 1 - kb0;                // keys after kb0 in the row
 #pragma unroll
       for (int kv = 0; kv < 2; ++kv)
 #pragma unroll
@@ -345,7 +387,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
   const int t_a = (mask_x + BN) / BN;
   const int mask_y = wl >= 0 ? p_last - wl - kstart : 0;
   const int t_b = mask_y > 0 ? (mask_y + BN - 1) / BN : 0;
-  auto needs_mask = [&](int t) { return t >= t_a || t < t_b; };
+  // Steps in [t_b, t_a) need no mask: one unsigned compare per step.
+  const uint32_t t_span = t_a > t_b ? (uint32_t)(t_a - t_b) : 0u;
+  auto needs_mask = [&](int t) { return (uint32_t)(t - t_b) >= t_span; };
   // Scores of keys outside [lo_j, hi_j] become -inf.
   auto apply_mask = [&](f32x4_t (&sacc)[NQB][2], int kbase) {
     const int k0 = kbase + 4 * lg;
@@ -411,7 +455,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
   // copies in flight.
   constexpr int NL = 2 * NI;  // copies per wave per step
 #pragma unroll
-  for (int t = 0; t < PF; ++t) issue(t, t);
+  for (int t = 0; t < PF; ++t) issue(t, t * BUFB);
   wait_copies<(PF - 1) * NL>();
   __syncthreads();
   f32x4_t sa[NQB][2], sb[NQB][2];
@@ -435,17 +479,20 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
   constexpr int NG = 2 * KSTEPS;         // K fragments per step (16 keys x 32 d)
   constexpr int NEA = 8 * NQB;           // exponentials per lane per step
   constexpr int KA = PKV_PREFILL_KA;     // fragment groups read ahead
-  // bi = i % NBUF, carried from step to step (no division).
-  auto step = [&](f32x4_t (&cur)[NQB][2], f32x4_t (&nxt)[NQB][2], int i, int bi) {
-    const int bn = bi + 1 == NBUF ? 0 : bi + 1;   // (i + 1) % NBUF
-    const int bp = bi == 0 ? NBUF - 1 : bi - 1;   // (i + PF) % NBUF = (i - 1) % NBUF
+  // bo = (i % NBUF) * BUFB, carried from step to step; NBUF is a power of
+  // two, so the ring wraps with a mask.
+  static_assert((NBUF & (NBUF - 1)) == 0, "ring offsets wrap with a mask");
+  constexpr uint32_t RING = NBUF * BUFB - 1;
+  auto step = [&](f32x4_t (&cur)[NQB][2], f32x4_t (&nxt)[NQB][2], int i, uint32_t bo) {
+    const uint32_t bn = (bo + BUFB) & RING;              // buffer of step i + 1
+    const uint32_t bp = (bo + (NBUF - 1) * BUFB) & RING;  // of step i + PF = i - 1 (mod NBUF)
     if constexpr (PRIO) __builtin_amdgcn_s_setprio(2);
     issue(i + PF, bp);
     if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     u32x4_t pb[NQB];
     // ---- S(i+1) on the matrix cores while the VALU turns S(i) into P ----
     {
-      const uint8_t* kp = sK + bn * BUFB + li * ROWB;
+      const uint8_t* kp = sK + bn + li * ROWB;
       // fragment g: keys 16 (g / KSTEPS) + li, logical segment 4 (g % KSTEPS) + lg
       auto kread = [&](int gi) {
         return *reinterpret_cast<const u32x4_t*>(
@@ -495,7 +542,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
     // ---- O += P V on the matrix cores while the VALU finds S(i+1)'s maxima ----
     float lm[NQB];
     {
-      const uint8_t* vb = sV + bi * BUFB + v_row * ROWB + v_h;
+      const uint8_t* vb = sV + bo + v_row * ROWB + v_h;
       auto vread = [&](int db) {
         const uint8_t* vp = vb + 16 * ((2 * db) ^ v_z);
         const u32x2_t v0 = lds_read_tr16(reinterpret_cast<const uint16_t*>(vp));
@@ -525,14 +572,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
     __syncthreads();
   };
 
-  int i = 0, bi = 0;
+  int i = 0;
+  uint32_t bo = 0;
   for (; i + 1 < ntiles; i += 2) {
-    step(sa, sb, i, bi);
-    bi = bi + 1 == NBUF ? 0 : bi + 1;
-    step(sb, sa, i + 1, bi);
-    bi = bi + 1 == NBUF ? 0 : bi + 1;
+    step(sa, sb, i, bo);
+    bo = (bo + BUFB) & RING;
+    step(sb, sa, i + 1, bo);
+    bo = (bo + BUFB) & RING;
   }
-  if (i < ntiles) step(sa, sb, i, bi);
+  if (i < ntiles) step(sa, sb, i, bo);
   // Copies of the clamped steps past the end may still be in flight: let them
   // land before the workgroup ends and its LDS goes to another.
   wait_copies<0>();
