@@ -446,6 +446,16 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
   const int v_row = 4 * lg + (li >> 2);
   const int v_z = vswz(v_row);  // equal for v_row + 16
   const int v_h = ((li & 3) >> 1) * 16 + (li & 1) * 8;
+  // Per-lane byte offsets inside a buffer of the K fragments (by k-step) and
+  // the V fragments (by 16-row block of head_dim), row base included: a step
+  // adds only its buffer's offset.
+  uint32_t k_ofs[KSTEPS], v_ofs[DBLK];
+#pragma unroll
+  for (int st = 0; st < KSTEPS; ++st)
+    k_ofs[st] = (uint32_t)(li * ROWB + 16 * ((4 * st + lg) ^ kswz(li)));
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+    v_ofs[db] = (uint32_t)(v_row * ROWB + v_h + 16 * ((2 * db) ^ v_z));
   // ---- pipeline ----
   // Step t's K and V are copied PF steps ahead, into buffer t % NBUF.  Step i
   // reads K(i+1) and V(i) and issues the copies of step i+PF, into the buffer
@@ -492,11 +502,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
     u32x4_t pb[NQB];
     // ---- S(i+1) on the matrix cores while the VALU turns S(i) into P ----
     {
-      const uint8_t* kp = sK + bn + li * ROWB;
+      const uint8_t* kp = sK + bn;
       // fragment g: keys 16 (g / KSTEPS) + li, logical segment 4 (g % KSTEPS) + lg
       auto kread = [&](int gi) {
-        return *reinterpret_cast<const u32x4_t*>(
-            kp + (gi / KSTEPS) * 16 * ROWB + 16 * ((4 * (gi % KSTEPS) + lg) ^ kswz(li)));
+        return *reinterpret_cast<const u32x4_t*>(kp + k_ofs[gi % KSTEPS] +
+                                                 (gi / KSTEPS) * 16 * ROWB);
       };
       u32x4_t kf[KA + 1];
 #pragma unroll
@@ -542,9 +552,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
     // ---- O += P V on the matrix cores while the VALU finds S(i+1)'s maxima ----
     float lm[NQB];
     {
-      const uint8_t* vb = sV + bo + v_row * ROWB + v_h;
+      const uint8_t* vb = sV + bo;
       auto vread = [&](int db) {
-        const uint8_t* vp = vb + 16 * ((2 * db) ^ v_z);
+        const uint8_t* vp = vb + v_ofs[db];
         const u32x2_t v0 = lds_read_tr16(reinterpret_cast<const uint16_t*>(vp));
         const u32x2_t v1 = lds_read_tr16(reinterpret_cast<const uint16_t*>(vp + 16 * ROWB));
         return u32x4_t{v0[0], v0[1], v1[0], v1[1]};
