@@ -271,7 +271,9 @@ pkv_status pkv_run(const pkv_plan* plan, const void* q, const void* kv_cache_lay
  *   pkv_plan_upload and pkv_run.  Dense plans are PKV_E_INVALID.
  * Every call on one GPU shares its array, which keeps the last call's contents:
  * calls that overlap on one GPU (different streams, or threads without ordering)
- * race.  Calls on one stream are ordered. */
+ * race.  Calls on one stream are ordered.  The plan's per-kernel timing
+ * (pkv_timing_enable) is not recorded for these calls (its events are created on
+ * first use). */
 pkv_status pkv_run_noalloc(pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
                            float* lse, void* stream);
 size_t pkv_noalloc_capacity(void);

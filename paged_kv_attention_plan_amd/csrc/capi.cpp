@@ -355,13 +355,17 @@ pkv_status check_run(const pkv_plan* plan, const void* q, const void* kv_cache_l
   return PKV_OK;
 }
 
-// Launch the plan's kernels (arguments already checked).
+// Launch the plan's kernels (arguments already checked).  timed: record the
+// plan's per-kernel timing events when timing is on (which may create events).
 pkv_status run_impl(const pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
-                    float* lse, void* workspace, void* stream) {
+                    float* lse, void* workspace, void* stream, bool timed = true) {
   const pkv::PlanData& d = plan->d;
   const pkv_plan_params& P = d.params;
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  auto mark = [&](int kind, bool begin) {
+    return timed ? timing_mark(plan, s, kind, begin) : hipSuccess;
+  };
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)P.head_dim));
   const int32_t* indices = reinterpret_cast<const int32_t*>(ws + d.ws.off_indices);
   float* part_o = reinterpret_cast<float*>(ws + d.ws.off_part_o);
@@ -416,13 +420,13 @@ pkv_status run_impl(const pkv_plan* plan, const void* q, const void* kv_cache_la
   // two write disjoint tokens); the merge of split decode rows follows.
   const bool fused = has_dec && has_pre && pkv::mixed_launch_fits(da, pa);
   if (fused) {
-    PKV_HIP(timing_mark(plan, s, kDecode, true));
+    PKV_HIP(mark(kDecode, true));
     PKV_HIP(pkv::launch_mixed(da, pa, s));
-    PKV_HIP(timing_mark(plan, s, kDecode, false));
+    PKV_HIP(mark(kDecode, false));
   } else if (has_dec) {
-    PKV_HIP(timing_mark(plan, s, kDecode, true));
+    PKV_HIP(mark(kDecode, true));
     PKV_HIP(pkv::launch_decode(da, s));
-    PKV_HIP(timing_mark(plan, s, kDecode, false));
+    PKV_HIP(mark(kDecode, false));
   }
   if (st ? d.caps.merges > 0 : !d.merges.empty()) {
     pkv::MergeArgs a{};
@@ -439,14 +443,14 @@ pkv_status run_impl(const pkv_plan* plan, const void* q, const void* kv_cache_la
     a.num_qo_heads = P.num_qo_heads;
     a.head_dim = P.head_dim;
     a.group = d.group;
-    PKV_HIP(timing_mark(plan, s, kMerge, true));
+    PKV_HIP(mark(kMerge, true));
     PKV_HIP(pkv::launch_merge(a, s));
-    PKV_HIP(timing_mark(plan, s, kMerge, false));
+    PKV_HIP(mark(kMerge, false));
   }
   if (has_pre && !fused) {
-    PKV_HIP(timing_mark(plan, s, kPrefill, true));
+    PKV_HIP(mark(kPrefill, true));
     PKV_HIP(pkv::launch_prefill(pa, s));
-    PKV_HIP(timing_mark(plan, s, kPrefill, false));
+    PKV_HIP(mark(kPrefill, false));
   }
   return PKV_OK;
 }
@@ -457,10 +461,10 @@ pkv_status run_impl(const pkv_plan* plan, const void* q, const void* kv_cache_la
 
 pkv_status pkv::detail::run_plan(const pkv_plan* plan, const void* q, const void* kv_cache_layer,
                                  void* out, float* lse, void* workspace, size_t workspace_bytes,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, bool timed) {
   pkv_status st = check_run(plan, q, kv_cache_layer, out, lse, workspace, workspace_bytes);
   if (st != PKV_OK || (plan->d.total_q == 0 && !plan->d.is_static)) return st;
-  return run_impl(plan, q, kv_cache_layer, out, lse, workspace, stream);
+  return run_impl(plan, q, kv_cache_layer, out, lse, workspace, stream, timed);
 }
 
 extern "C" {
@@ -469,7 +473,7 @@ pkv_status pkv_run(const pkv_plan* plan, const void* q, const void* kv_cache_lay
                    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   return pkv::detail::run_plan(plan, q, kv_cache_layer, out, lse, workspace, workspace_bytes,
-                               static_cast<hipStream_t>(stream));
+                               static_cast<hipStream_t>(stream), true);
 }
 
 pkv_status pkv_run_append(const pkv_plan* plan, const void* q, const void* k_new, const void* v_new,

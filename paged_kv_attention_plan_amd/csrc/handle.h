@@ -41,9 +41,11 @@ void clear_error();
 pkv_status upload_meta(pkv_plan* plan, void* workspace, size_t workspace_bytes, hipStream_t stream,
                        bool may_allocate);
 
-// Argument checks of pkv_run, then its launches.
+// Argument checks of pkv_run, then its launches.  timed = false skips the
+// plan's per-kernel timing events (their lazy creation allocates).
 pkv_status run_plan(const pkv_plan* plan, const void* q, const void* kv_cache_layer, void* out,
-                    float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+                    float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                    bool timed);
 
 }  // namespace detail
 }  // namespace pkv

@@ -71,7 +71,10 @@ pkv_status pkv_run_noalloc(pkv_plan* plan, const void* q, const void* kv_cache_l
   // whole metadata region and every partial is written before it is read.
   st = pkv::detail::upload_meta(plan, ws, kScratchBytes, s, /*may_allocate=*/false);
   if (st != PKV_OK) return st;
-  return pkv::detail::run_plan(plan, q, kv_cache_layer, out, lse, ws, kScratchBytes, s);
+  // The plan's per-kernel timing (pkv_timing_enable) is not recorded here: its
+  // events are created on first use.
+  return pkv::detail::run_plan(plan, q, kv_cache_layer, out, lse, ws, kScratchBytes, s,
+                               /*timed=*/false);
 }
 
 }  // extern "C"

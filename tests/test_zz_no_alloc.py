@@ -76,14 +76,20 @@ def test_noalloc_matches_upload_and_run(pkv, gpu, name):
         # plan's staging buffers on the first step)
         ws = torch.empty(plan.ws_bytes, dtype=torch.uint8, device=gpu)
         pkv.plan_upload(plan, ws)
+        # with the plan's own timing on, pkv_run records its launches and
+        # pkv_run_noalloc records none (its events would be created on first use)
+        pkv.timing_enable(plan)
         out_ref = torch.full_like(q, float("nan"))
         lse_ref = torch.full((q.shape[0], w.num_qo_heads), float("nan"), device=gpu)
         pkv.run(plan, q, w.cache, out_ref, ws, lse=lse_ref)
+        assert sum(n for _, n in pkv.timing_read(plan).values()) > 0
         # the static workspace
         out = torch.full_like(q, float("nan"))
         lse = torch.full((q.shape[0], w.num_qo_heads), float("nan"), device=gpu)
         pkv.run_noalloc(plan, q, w.cache, out, lse=lse)
         torch.cuda.synchronize()
+        assert sum(n for _, n in pkv.timing_read(plan).values()) == 0
+        pkv.timing_enable(plan, False)
         say(f"  step {k}: {len(rows)} rows, {q.shape[0]} queries, workspace {plan.ws_bytes} bytes")
         assert torch.equal(out.view(torch.int16), out_ref.view(torch.int16)), "out bits differ"
         assert torch.equal(lse.view(torch.int32), lse_ref.view(torch.int32)), "lse bits differ"
