@@ -76,7 +76,8 @@ extern "C" {
 typedef enum pkv_status {
   PKV_OK = 0,
   PKV_E_INVALID = 1,      /* malformed page table, bad argument, q_len > kv_len, kv_lens mismatch */
-  PKV_E_UNSUPPORTED = 2,  /* head_dim, dtype, page_size or group size this build does not compute */
+  PKV_E_UNSUPPORTED = 2,  /* head_dim, dtype, page_size or group size this build does not compute,
+                             or a page of K and V of 2 GiB or more */
   PKV_E_WORKSPACE = 3,    /* workspace smaller than the plan needs; message gives the bytes */
   PKV_E_CAPACITY = 4,     /* more prompt rows than max_prefill_rows (mixed step) */
   PKV_E_CONFLICT = 5,     /* two appended tokens map to one cache slot */

@@ -167,6 +167,12 @@ pkv_status check_params(const pkv_plan_params& p, std::string& err) {
     err = "page_size must be a power of two in [1, 256] (got " + std::to_string(p.page_size) + ")";
     return PKV_E_UNSUPPORTED;
   }
+  // The kernels address K and V inside a page with 32-bit offsets.
+  if (2 * (int64_t)p.page_size * p.num_kv_heads * p.head_dim * 2 >= (int64_t(1) << 31)) {
+    err = "a page of K and V (2 x page_size x num_kv_heads x head_dim bf16) must stay under 2 GiB "
+          "(num_kv_heads " + std::to_string(p.num_kv_heads) + ")";
+    return PKV_E_UNSUPPORTED;
+  }
   if (p.window_left < -1) {
     err = "window_left must be -1 (unbounded) or >= 0";
     return PKV_E_INVALID;

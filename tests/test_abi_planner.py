@@ -230,6 +230,19 @@ def test_errors_unsupported_head_dim_and_page_size():
     assert _err(lambda: pkv.plan_create(p, None, w.kv_indptr, w.kv_indices, w.last_page_len)) == pkv.E_UNSUPPORTED
 
 
+def test_error_page_over_2gib():
+    """Pages are addressed with 32-bit offsets: 2 * page_size * Hk * D * 2 bytes
+    must stay under 2 GiB (page 256, D 128: Hk below 16384)."""
+    w = _tiny()
+    p = _params(w, "decode")
+    p.page_size, p.head_dim = 256, 128
+    p.num_kv_heads, p.num_qo_heads = 16384, 16384
+    assert _err(lambda: pkv.plan_create(p, None, w.kv_indptr, w.kv_indices, w.last_page_len)) == pkv.E_UNSUPPORTED
+    assert "2 GiB" in pkv._lib.pkv_last_error().decode()
+    p.num_kv_heads, p.num_qo_heads = 16383, 16383
+    pkv.plan_create(p, None, w.kv_indptr, w.kv_indices, w.last_page_len)
+
+
 @pytest.mark.parametrize("bad", ["lpl0", "lpl_big", "no_pages", "page_oob", "kv_lens", "heads"])
 def test_errors_invalid_page_table(bad):
     w = _tiny()
