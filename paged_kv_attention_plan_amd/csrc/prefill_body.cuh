@@ -253,8 +253,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
 
   // Copy map: copy j of wave w fills rows KW*w + RPI*j + lane/SEGS of the step,
   // physical segment lane % SEGS, with the source segment that the swizzle
-  // puts there.  src_k/src_v: the lane's byte offset inside a key row.
-  // (recomputed at each issue: a few VALU per step instead of 3*NI live registers)
+  // puts there; copy_src gives the lane's byte offset inside a key row.  (On
+  // the steps whose keys all lie in the row the lanes' offsets do not change,
+  // so they stay in registers; the row-end steps clamp them.)
   auto copy_src = [&](int j, bool v, int& rwj) -> uint32_t {
     rwj = RPI * j + lane / SEGS;
     const int r = KW * wave + rwj;
@@ -266,8 +267,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int tile) {
   // Issue the copies of step t (clamped to the last step, and each key to the
   // row's last key, so addresses stay inside the row; keys past the row are
   // masked later) into the buffer at byte offset boff (t % NBUF times BUFB) of
-  // the K and V rings.  Every call issues exactly 2*NI copies
-  // per wave: the waits below count on it.
+  // the K and V rings.  Every call issues exactly 2*NI copies per wave: the
+  // waits below count on it.
   auto issue = [&](int t, uint32_t boff) {
     const uint32_t mk = (uint32_t)__builtin_amdgcn_readfirstlane(
         (int)(lds_k + boff + KW * wave * ROWB));
